@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming attention hot path on one MI355X.
+
+One step = one pass of the whole path on resident synthetic inputs:
+  * causal GQA prefill, Llama3-70B head shape: B=1, 64 query / 8 KV heads,
+    S=8192, d=128, bf16 (attn_prefill), and
+  * split-KV GQA decode: B=4, 64/8 heads, KV cache 32768 tokens, d=128, bf16,
+    64 splits per sequence (attn_decode_splitkv + attn_combine_lse).
+
+Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s
+(4 * d * visible (q, k) pairs per head / prefill kernel time); the decode
+throughput in KV GB/s (every valid K and V byte once / split + combine time)
+is reported next to it.  Kernel times come from HIP events recorded on the
+stream the kernels run on, over the timed steps.  The float64 oracle, timed on
+the host cores on a bounded sample of the same prefill workload, is reported as
+`cpu_baseline` (a baseline only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (dense bf16)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQA"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(target_s: float):
+    """Time the float64 oracle on whole query heads of the prefill workload
+    (all 8192 rows of head 0, 1, ... until about target_s seconds)."""
+    import oracle
+    from streaming_attention_amd import workloads as W
+
+    w = W.GQA70B_PREFILL
+    q, k, v = W.prefill_inputs(w, "cpu")          # the same seeded inputs as the GPU leg
+    kh = k[:, 0:1].float().numpy()
+    vh = v[:, 0:1].float().numpy()
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        qh = q[:, heads:heads + 1].float().numpy()   # query heads of KV head 0
+        oracle.attention(qh, kh, vh, w.scale, True)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or heads >= w.Hq // w.Hkv:
+            break
+    flops = 4 * w.d * w.visible_pairs_per_head() * heads
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 0)) for i in info) or threads
+    except Exception:
+        pass
+    return {
+        "value": round(flops / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"float64 oracle (score matrix materialised), {heads} query head(s) x all {w.Sq} rows "
+                  f"of the causal S={w.Skv} d={w.d} prefill, {el:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(no collectives or multi-GPU sharding in this library).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import streaming_attention_amd as sa
+    from streaming_attention_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wp = W.GQA70B_PREFILL
+    wd = W.GQA70B_DECODE
+
+    q, k, v = W.prefill_inputs(wp, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wp.B, wp.Hq, wp.Sq), dtype=torch.float32, device=dev)
+    qd, kc, vc, lens = W.decode_inputs(wd, dev)
+    part_o = torch.empty((wd.B, wd.Hq, wd.splits, wd.d), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((wd.B, wd.Hq, wd.splits), dtype=torch.float32, device=dev)
+    od = torch.empty((wd.B, wd.Hq, 1, wd.d), dtype=torch.bfloat16, device=dev)
+    lsed = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        sa.prefill(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
+        if i is not None:
+            ev[i][1].record(stream)
+        sa.decode(qd, kc, vc, None, None, max_splits=wd.splits, scale=wd.scale,
+                  part_o=part_o, part_lse=part_lse, out=od, lse=lsed)
+        if i is not None:
+            ev[i][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pf_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)) / n_ev
+    dc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)) / n_ev
+    ms_step = wall * 1e3 / args.steps
+
+    pf_flops = wp.flops()
+    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+    kv_bytes = W.decode_kv_bytes(lens, wd.Hkv, wd.d)
+    dc_gbs = kv_bytes / (dc_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(pf_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "70B-shape GQA step: causal prefill B=1 Hq=64 Hkv=8 S=8192 d=128 bf16 "
+                        "+ split-KV decode B=4 Hq=64 Hkv=8 KV=32768 d=128 bf16, 64 splits",
+            "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Skv": wp.Skv, "d": wp.d,
+                        "causal": True, "algorithmic_tflop": round(pf_flops / 1e12, 6)},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "kv_len": wd.fixed_len, "d": wd.d,
+                       "splits": wd.splits, "kv_bytes": kv_bytes},
+        },
+        "prefill": {"ms": round(pf_ms, 4), "tflops": round(pf_tflops, 2),
+                    "pct_mfma_peak": round(100 * pf_tflops / MFMA_BF16_PEAK_TFLOPS, 2)},
+        "decode": {"us": round(dc_ms * 1e3, 2), "kv_gbs": round(dc_gbs, 1),
+                   "pct_hbm_peak": round(100 * dc_gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_bf16_kernel<128,causal>",
+            "achieved": round(pf_tflops, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "roofline_decode": {
+            "bound": "hbm",
+            "kernel": "decode_splitkv_bf16_kernel<128> + combine_lse_kernel",
+            "achieved": round(dc_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dc_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        del q, k, v, o, lse, qd, kc, vc, part_o, part_lse, od, lsed
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

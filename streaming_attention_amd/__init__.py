@@ -1,0 +1,18 @@
+"""Streaming attention forward for AMD Instinct MI355X (gfx950).
+
+Fused prefill (GQA, causal), split-KV decode and the log-sum-exp combine, as
+hand-written HIP kernels behind the C ABI in ``include/attn.h``.  This package
+is the thin Python binding over ``libattn.so`` plus the seeded workloads.
+"""
+
+from ._binding import (  # noqa: F401
+    AttnError,
+    LIB_PATH,
+    combine_lse,
+    decode,
+    decode_splitkv,
+    lib,
+    prefill,
+    splits_for_lengths,
+)
+from . import workloads  # noqa: F401

@@ -1,0 +1,215 @@
+"""ctypes binding of ``libattn.so`` -- argument marshalling only.
+
+Every step of the attention computation runs in the library's HIP kernels; this
+module checks tensor metadata, allocates outputs with torch (device memory),
+passes raw pointers and torch's current HIP stream, and turns a non-zero
+status into an exception.  There is no fallback: if the library is missing or
+a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+_DTYPE_CODE = {torch.float32: ATTN_DTYPE_F32, torch.bfloat16: ATTN_DTYPE_BF16}
+
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_LAUNCH"}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+SIGNATURES = {
+    "attn_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P], ctypes.c_int),
+    "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], ctypes.c_int),
+    "attn_combine_lse": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], ctypes.c_int),
+    "attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = STATUS.get(status, f"status {status}")
+        try:
+            msg += ": " + lib().attn_status_string(status).decode()
+        except Exception:  # pragma: no cover
+            pass
+        super().__init__(f"{where}: {msg}")
+
+
+def lib():
+    """Load ``libattn.so`` (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m streaming_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, ndim, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check(status, where):
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True):
+    """Fused streaming attention forward (``attn_prefill``).
+
+    ``q [B,Hq,Sq,d]``, ``k, v [B,Hkv,Skv,d]``, bf16 or fp32, contiguous, on one
+    GPU.  Causal alignment is bottom-right (the queries are the last Sq
+    positions).  Returns ``(o, lse)`` or ``o``.
+    """
+    _need(q, "q", 4)
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    _need(k, "k", 4, dt, q.device)
+    _need(v, "v", 4, dt, q.device)
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Skv, d) or tuple(v.shape) != (B, Hkv, Skv, d):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", 4, dt, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", 3, torch.float32, q.device)
+        if tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError("lse must be [B,Hq,Sq]")
+    st = lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, d,
+                            _DTYPE_CODE[dt], 1 if causal else 0, float(scale), _stream(q))
+    _check(st, "attn_prefill")
+    return (out, lse) if return_lse else out
+
+
+def decode_splitkv(q, k_cache, v_cache, kv_len=None, num_splits=None, max_splits: int = 64,
+                   scale: float | None = None, part_o=None, part_lse=None):
+    """Split-KV decode partials (``attn_decode_splitkv``).
+
+    ``q [B,Hq,1,d]`` bf16, caches ``[B,Hkv,S_cap,d]`` bf16, ``kv_len`` and
+    ``num_splits`` int32 GPU tensors ``[B]`` or None.  Returns
+    ``(part_o [B,Hq,max_splits,d] f32, part_lse [B,Hq,max_splits] f32)``.
+    """
+    _need(q, "q", 4, torch.bfloat16)
+    _need(k_cache, "k_cache", 4, torch.bfloat16, q.device)
+    _need(v_cache, "v_cache", 4, torch.bfloat16, q.device)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per sequence: q must be [B,Hq,1,d]")
+    Hkv, S_cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, S_cap, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    for name, t in (("kv_len", kv_len), ("num_splits", num_splits)):
+        if t is not None:
+            _need(t, name, 1, torch.int32, q.device)
+            if t.shape[0] != B:
+                raise ValueError(f"{name} must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if part_o is None:
+        part_o = torch.empty((B, Hq, max_splits, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, max_splits), dtype=torch.float32, device=q.device)
+    _need(part_o, "part_o", 4, torch.float32, q.device)
+    _need(part_lse, "part_lse", 3, torch.float32, q.device)
+    if tuple(part_o.shape) != (B, Hq, max_splits, d) or tuple(part_lse.shape) != (B, Hq, max_splits):
+        raise ValueError("partial buffers must be [B,Hq,max_splits,d] and [B,Hq,max_splits]")
+    st = lib().attn_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(num_splits),
+                                   B, Hq, Hkv, S_cap, d, int(max_splits), ATTN_DTYPE_BF16, float(scale),
+                                   _ptr(part_o), _ptr(part_lse), _stream(q))
+    _check(st, "attn_decode_splitkv")
+    return part_o, part_lse
+
+
+def combine_lse(part_o, part_lse, num_splits=None, out_dtype=torch.bfloat16, out=None, lse=None):
+    """Log-sum-exp merge of split partials (``attn_combine_lse``).
+
+    Returns ``(o [B,Hq,1,d] out_dtype, lse [B,Hq] f32)``.
+    """
+    _need(part_o, "part_o", 4, torch.float32)
+    B, Hq, max_splits, d = part_o.shape
+    _need(part_lse, "part_lse", 3, torch.float32, part_o.device)
+    if tuple(part_lse.shape) != (B, Hq, max_splits):
+        raise ValueError("part_lse must be [B,Hq,max_splits]")
+    if num_splits is not None:
+        _need(num_splits, "num_splits", 1, torch.int32, part_o.device)
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    if out is None:
+        out = torch.empty((B, Hq, 1, d), dtype=out_dtype, device=part_o.device)
+    _need(out, "out", 4, out_dtype, part_o.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=part_o.device)
+    _need(lse, "lse", 2, torch.float32, part_o.device)
+    st = lib().attn_combine_lse(_ptr(part_o), _ptr(part_lse), _ptr(num_splits), B, Hq, max_splits, d,
+                                _ptr(out), _ptr(lse), _DTYPE_CODE[out_dtype], _stream(part_o))
+    _check(st, "attn_combine_lse")
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, kv_len=None, num_splits=None, max_splits: int = 64,
+           scale: float | None = None, part_o=None, part_lse=None, out=None, lse=None):
+    """Split-KV decode followed by the log-sum-exp combine: ``(o, lse)``."""
+    po, pl = decode_splitkv(q, k_cache, v_cache, kv_len, num_splits, max_splits, scale, part_o, part_lse)
+    return combine_lse(po, pl, num_splits, q.dtype, out, lse)
+
+
+def splits_for_lengths(lens, keys_per_split: int = 2048, max_splits: int = 64):
+    """Split count per sequence: ``min(max_splits, max(1, ceil(len / keys_per_split)))``.
+
+    A tuning choice (the pages leave the one-shot vs tiled crossover open); any
+    split count gives the same result up to rounding.
+    """
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    n = (lens + keys_per_split - 1) // keys_per_split
+    return n.clamp(1, max_splits).to(torch.int32)

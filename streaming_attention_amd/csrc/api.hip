@@ -1,0 +1,106 @@
+// C ABI of the streaming attention library: argument validation on the host,
+// then one enqueue on the caller's stream.  See include/attn.h for the
+// contract of every entry point.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr long long kMaxGrid = (1LL << 24) - 1;   // workgroups per launch (x 256 threads < 2^32)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid size, scale or causal/size relation";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head dim or head grouping";
+    case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
+                 int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d, int32_t dtype, int32_t causal, float scale,
+                 void* stream) {
+  if (B < 0 || Sq < 0 || Skv < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (!good_scale(scale)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+  const long long G = Hq / Hkv;
+  if (G * (long long)Sq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const long long n_mt = (G * Sq + 127) / 128;
+  if (n_mt * (long long)B * Hkv > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (Skv > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_ERR_ALIGN;
+
+  sa::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Skv = Skv; a.d = d;
+  a.bf16 = dtype == ATTN_DTYPE_BF16;
+  a.causal = causal != 0;
+  a.scale = scale;
+  return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                        const int32_t* num_splits, int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
+                        int32_t max_splits, int32_t dtype, float scale, float* part_o, float* part_lse,
+                        void* stream) {
+  if (B < 0 || S_cap < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
+  if (!good_scale(scale)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv * max_splits > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (B == 0) return ATTN_OK;
+  if (q == nullptr || part_o == nullptr || part_lse == nullptr) return ATTN_ERR_NULL;
+  if (S_cap > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(part_o) || !aligned16(part_lse) ||
+      (S_cap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return ATTN_ERR_ALIGN;
+
+  sa::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_len = kv_len; a.num_splits = num_splits;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_cap = S_cap; a.d = d; a.max_splits = max_splits;
+  a.scale = scale; a.part_o = part_o; a.part_lse = part_lse;
+  return sa::launch_decode_splitkv(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+                                                                                            : ATTN_ERR_LAUNCH;
+}
+
+int attn_combine_lse(const float* part_o, const float* part_lse, const int32_t* num_splits, int32_t B,
+                     int32_t Hq, int32_t max_splits, int32_t d, void* o, float* lse, int32_t out_dtype,
+                     void* stream) {
+  if (B < 0 || Hq < 1) return ATTN_ERR_SHAPE;
+  if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+  if (((long long)B * Hq + 3) / 4 > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (B == 0) return ATTN_OK;
+  if (part_o == nullptr || part_lse == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (!aligned16(part_o) || !aligned16(part_lse) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+
+  sa::CombineArgs a;
+  a.part_o = part_o; a.part_lse = part_lse; a.num_splits = num_splits;
+  a.B = B; a.Hq = Hq; a.max_splits = max_splits; a.d = d;
+  a.o = o; a.lse = lse; a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
+  return sa::launch_combine_lse(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+                                                                                        : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

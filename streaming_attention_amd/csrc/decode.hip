@@ -1,0 +1,285 @@
+// Split-KV decode for gfx950: one query token per sequence, the valid key
+// range cut into contiguous splits, one normalised partial (lse, O) per split.
+//
+// Method: "ADR-0060: AHBM GQA Fused Attention kernel (Llama3-70B)", section
+// 5.2 (decode attends to all past keys, only the ragged last tile is masked;
+// the G query rows of a KV head are stacked into the GEMM M dimension so each
+// K/V byte is read once for all of them), sections 4 and 5.3 (each split sweeps
+// its own key range with the per-tile online softmax of section 3 and yields
+// (m_i, l_i, O_i)), section 2.1 (splits are contiguous key blocks).
+//
+// MI355X mapping
+//   * One workgroup per (sequence, KV head, split), 4 waves.  The split's keys
+//     are taken 32 at a time; wave w handles chunks w, w + 4, ...  Each wave
+//     keeps its own running (m, l, O) and double-buffers its next chunk's K and
+//     V in registers, so every wave has 16 KB of loads in flight while it
+//     computes.  At the end the four wave states are merged through LDS with
+//     the same log-sum-exp rule as the split merge.
+//   * Scores are S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from global
+//     memory straight into the A operand, Q of the G <= 16 heads as the B
+//     operand, zero-padded to 16 columns).  Each lane owns one query column and
+//     8 of the chunk's 32 keys; the other keys of that query sit in lanes
+//     l ^ 16, l ^ 32, l ^ 48.
+//   * O^T += V^T P^T: P^T is 8 accumulator registers of S^T rounded to bf16;
+//     V^T comes from a per-wave LDS region that V is written into transposed
+//     (8-byte writes of 4 keys, key order permuted to match P^T).
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 32;          // keys per wave iteration
+constexpr int kSplitGranule = 64;   // split boundaries are multiples of this
+
+template <int D>
+struct DecodeCfg {
+  static constexpr int DS = D / 32;          // S^T MFMA steps over d
+  static constexpr int DB = D / 16;          // 16-row d blocks of O^T
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int LQ = 64 / CPR;        // lanes sharing a chunk column
+  static constexpr int NGRP = 8 / LQ;        // 4-key groups per lane (2 or 1)
+  static constexpr int VTP = kChunk + 8;     // V^T row pitch (elements), 80 B
+  static constexpr int VT_ELEMS = D * VTP;   // per wave
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ num_splits, int B, int Hq,
+    int Hkv, int S_cap, int max_splits, float c, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
+  using C = DecodeCfg<D>;
+  constexpr int MERGE_FLOATS = 4 * 16 * D + 2 * 4 * 16;
+  constexpr int SMEM_BYTES_VT = 4 * C::VT_ELEMS * 2;
+  constexpr int SMEM_BYTES = SMEM_BYTES_VT > MERGE_FLOATS * 4 ? SMEM_BYTES_VT : MERGE_FLOATS * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
+
+  const int wg = blockIdx.x;
+  const int s = wg % max_splits;
+  const int kvh = (wg / max_splits) % Hkv;
+  const int b = wg / (max_splits * Hkv);
+  const int G = Hq / Hkv;
+
+  int len = kv_len ? kv_len[b] : S_cap;
+  len = len < 0 ? 0 : (len > S_cap ? S_cap : len);
+  int n = num_splits ? num_splits[b] : max_splits;
+  n = n < 1 ? 1 : (n > max_splits ? max_splits : n);
+  if (s >= n) return;
+  const int per = (len + n - 1) / n;
+  const long long chunk = (long long)((per + kSplitGranule - 1) / kSplitGranule) * kSplitGranule;
+  const long long lo_ll = (long long)s * chunk;
+  const int lo = lo_ll < len ? (int)lo_ll : len;
+  const int hi = (int)((lo_ll + chunk) < len ? (lo_ll + chunk) : len);
+
+  const int tid = threadIdx.x;
+  const size_t head0 = (size_t)b * Hq + (size_t)kvh * G;
+  if (lo >= hi) {
+    // Empty split: (lse, O) = (-inf, 0).
+    for (int i = tid; i < G * D; i += kThreads) {
+      const int j = i / D, d = i % D;
+      part_o[((head0 + j) * max_splits + s) * D + d] = 0.f;
+      if (d == 0) part_lse[(head0 + j) * max_splits + s] = kNegInf;
+    }
+    return;
+  }
+
+  const int w = tid >> 6, l = tid & 63;
+  const int j16 = l & 15;     // query column of this lane
+  const int qq = l >> 4;      // which 4-key group of each 16-key block
+  const size_t kvoff = ((size_t)b * Hkv + kvh) * (size_t)S_cap * D;
+  const bf16* kg = kc + kvoff;
+  const bf16* vg = vc + kvoff;
+
+  // Q^T B operand: lane holds Q[head j16][32 s + 8 qq .. +7], zero past G.
+  bf16x8 qf[C::DS];
+#pragma unroll
+  for (int st = 0; st < C::DS; ++st) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (j16 < G) x = ld16(q + (head0 + j16) * D + 32 * st + 8 * qq);
+    qf[st] = as_bf16x8(x);
+  }
+
+  // V staging map: chunk column vcol (d = 8 vcol .. +7), key groups vgrp[g].
+  const int vcol = l / C::LQ;
+  const int vsub = l % C::LQ;
+
+  struct Regs {
+    u32x4 k[2][C::DS];
+    u32x4 v[C::NGRP][4];
+  };
+
+  auto load_chunk = [&](Regs& R, int key0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = key0 + 16 * kb + j16;
+#pragma unroll
+      for (int st = 0; st < C::DS; ++st) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (key < hi) x = ld16(kg + (size_t)key * D + 32 * st + 8 * qq);
+        R.k[kb][st] = x;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < C::NGRP; ++g) {
+      const int kgid = vsub + C::LQ * g;   // 4-key group index 0..7 inside the chunk
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 4 * kgid + r;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (key < hi) x = ld16(vg + (size_t)key * D + 8 * vcol);
+        R.v[g][r] = x;
+      }
+    }
+  };
+
+  bf16* VT = reinterpret_cast<bf16*>(smem) + w * C::VT_ELEMS;
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 oacc[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = (hi - lo + kChunk - 1) / kChunk;
+  Regs cur, nxt;
+  int ci = w;
+  if (ci < nch) load_chunk(cur, lo + ci * kChunk);
+  for (; ci < nch; ci += 4) {
+    if (ci + 4 < nch) load_chunk(nxt, lo + (ci + 4) * kChunk);
+    const int key0 = lo + ci * kChunk;
+
+    // S^T for keys key0 + 16 kb + (0..15).
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < C::DS; ++st)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[kb][st]), qf[st], sacc[kb], 0, 0, 0);
+    }
+    if (key0 + kChunk > hi) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * kb + 4 * qq + r;
+          sacc[kb][r] = key < hi ? sacc[kb][r] : kNegInf;
+        }
+    }
+
+    // V -> LDS, transposed: row d, key position 8 q + 4 kb + r.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < C::NGRP; ++g) {
+      const int kgid = vsub + C::LQ * g;
+      const int p0 = 8 * (kgid & 3) + 4 * (kgid >> 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dw = e >> 1;
+        uint32_t a, bq;
+        if (e & 1) {
+          a = pack_hi(cur.v[g][0][dw], cur.v[g][1][dw]);
+          bq = pack_hi(cur.v[g][2][dw], cur.v[g][3][dw]);
+        } else {
+          a = pack_lo(cur.v[g][0][dw], cur.v[g][1][dw]);
+          bq = pack_lo(cur.v[g][2][dw], cur.v[g][3][dw]);
+        }
+        u32x2 pr = {a, bq};
+        *reinterpret_cast<u32x2*>(VT + (8 * vcol + e) * C::VTP + p0) = pr;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // Online softmax over the chunk (base 2), row reduction over the 4 lanes
+    // that share this query column.
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float corr = exp2_hw(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
+        sacc[kb][r] = p;
+        psum += p;
+      }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    const bf16x8 pf = to_bf16x8(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3], sacc[1][0], sacc[1][1],
+                                sacc[1][2], sacc[1][3]);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      oacc[db] *= corr;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(VT + (16 * db + j16) * C::VTP + 8 * qq);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[db], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+
+  // Row sum over the 4 lanes of the query column.
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // Merge the 4 wave states through LDS.
+  __syncthreads();
+  float* Ow = reinterpret_cast<float*>(smem);       // [4][16][D] unnormalised O
+  float* mw = Ow + 4 * 16 * D;                        // [4][16]
+  float* lw = mw + 4 * 16;                            // [4][16]
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ow[(w * 16 + j16) * D + 16 * db + 4 * qq + r] = oacc[db][r];
+  if (l < 16) {
+    mw[w * 16 + l] = m_run;
+    lw[w * 16 + l] = l_run;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int j = i / D, d = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mw[ww * 16 + j]);
+    float osum = 0.f, wsum = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = exp2_hw(mw[ww * 16 + j] - M);
+        wsum += f * lw[ww * 16 + j];
+        osum += f * Ow[(ww * 16 + j) * D + d];
+      }
+    }
+    const bool has = wsum > 0.f;
+    part_o[((head0 + j) * max_splits + s) * D + d] = has ? osum / wsum : 0.f;
+    if (d == 0) part_lse[(head0 + j) * max_splits + s] = has ? (M + __log2f(wsum)) * kLn2 : kNegInf;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t stream) {
+  const long long grid = (long long)a.B * a.Hkv * a.max_splits;
+  const float c = a.scale * kLog2e;
+  const dim3 g((unsigned)grid), blk(kThreads);
+  if (a.d == 128)
+    hipLaunchKernelGGL((decode_splitkv_bf16_kernel<128>), g, blk, 0, stream, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, a.kv_len, a.num_splits, a.B, a.Hq, a.Hkv, a.S_cap, a.max_splits, c,
+                       a.part_o, a.part_lse);
+  else
+    hipLaunchKernelGGL((decode_splitkv_bf16_kernel<64>), g, blk, 0, stream, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, a.kv_len, a.num_splits, a.B, a.Hq, a.Hkv, a.S_cap, a.max_splits, c,
+                       a.part_o, a.part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace sa

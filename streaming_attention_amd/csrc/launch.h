@@ -1,0 +1,48 @@
+// Host-side launch interfaces between the C ABI layer and the kernel files.
+// Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Skv, d;
+  bool bf16;
+  bool causal;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* kv_len;
+  const int32_t* num_splits;
+  int B, Hq, Hkv, S_cap, d, max_splits;
+  float scale;
+  float* part_o;
+  float* part_lse;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* num_splits;
+  int B, Hq, max_splits, d;
+  void* o;
+  float* lse;
+  bool out_bf16;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine_lse(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,541 @@
+// Fused streaming attention forward (prefill) for gfx950.
+//
+// Method: "ADR-0060: AHBM GQA Fused Attention kernel (Llama3-70B)", section 3
+// (per KV tile: scores, boundary mask, tile max, new running max, P = exp(S - m),
+// correction exp(m_old - m_new), l = l*corr + rowsum P, O = O*corr + P V),
+// section 5.2 (the G query heads of one KV head stacked into the GEMM M
+// dimension, so one K/V tile serves all of them) and section 5.4 (tiles wholly
+// after the query block skipped, straddling tiles masked).  "AttentionRegion
+// Transformation" sections 6-8 give the same loop: Q tile resident, K/V tiles
+// streamed HBM -> shared memory -> registers, S and P never written out.
+//
+// MI355X mapping (bf16 path)
+//   * One workgroup = 4 waves = 128 stacked query rows of one (batch, KV head);
+//     each wave owns 32 rows.  KV tiles of 64 keys are staged through LDS,
+//     double buffered, with the next tile's global loads in flight while the
+//     current tile is computed (one barrier per tile).
+//   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     K (from LDS) is the A operand and Q (held in VGPRs for the whole sweep)
+//     the B operand.  In the accumulator layout every lane then owns ONE query
+//     row (column l % 32) and 32 of the tile's 64 keys; its partner lane l ^ 32
+//     holds the other 32.  Running max, running sum and the output rescale are
+//     therefore per-lane scalars, and a row reduction is a local reduction plus
+//     one exchange with the partner lane.
+//   * The output is accumulated transposed too, O^T += V^T P^T: V^T (from LDS)
+//     is the A operand, P^T the B operand.  The B operand of an MFMA needs, per
+//     lane, 8 consecutive reduction (key) indices of one query -- exactly 8
+//     consecutive accumulator registers of S^T, so P goes from the score
+//     accumulators to the P V operand with no data movement.  V is written to
+//     LDS transposed, with its key index permuted (bits 2 and 3 swapped) so that
+//     those 8 keys sit in 16 contiguous bytes of a V^T row.
+//   * Softmax runs in base 2: c = scale * log2(e) is folded into one FMA before
+//     v_exp_f32.  Masks are selects to -inf, never additions.
+//   * Work order: heaviest causal tiles first, and when the number of
+//     (batch, KV head) groups is a multiple of 8, every group's tiles go to one
+//     XCD (workgroups are dealt to the 8 XCDs round robin) so its K/V stays in
+//     that XCD's L2.
+//
+// fp32 path: the same loop with v_mfma_f32_32x32x2_f32 (one K value per lane
+// per step, so V needs no transpose) and 32-key tiles, P kept in fp32.
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+constexpr int kBM = 128;   // stacked query rows per workgroup
+constexpr int kBN = 64;    // keys per KV tile (bf16 path)
+constexpr int kThreads = 256;
+
+// Permutation of a key index inside a 64-key tile for the V^T layout in LDS:
+// swap bits 2 and 3.
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+struct TileCoord {
+  int b, kvh, mt;
+};
+
+// Workgroup index -> (batch, KV head, M tile).  Heaviest M tiles (latest query
+// positions) are dealt first; with n_groups % 8 == 0 each group is pinned to
+// XCD (group % 8).
+__device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int Hkv, int n_mt, int G,
+                                              int Sq) {
+  int group, rk;
+  if ((n_groups & 7) == 0) {
+    const int xcd = wg & 7, slot = wg >> 3, gpx = n_groups >> 3;
+    group = (slot % gpx) * 8 + xcd;
+    rk = slot / gpx;
+  } else {
+    group = wg % n_groups;
+    rk = wg / n_groups;
+  }
+  int mt;
+  if (Sq % kBM == 0) {
+    const int n_pb = Sq / kBM;         // position blocks per query head
+    const int pb = n_pb - 1 - rk / G;  // latest positions first
+    const int g = rk % G;
+    mt = g * n_pb + pb;
+  } else {
+    mt = n_mt - 1 - rk;
+  }
+  TileCoord t;
+  t.b = group / Hkv;
+  t.kvh = group % Hkv;
+  t.mt = mt;
+  return t;
+}
+
+// First / last valid stacked row of a row range and the smallest / largest
+// query position t (row % Sq) inside it.
+__device__ __forceinline__ void row_range_positions(int rA, int rB, int Sq, int& t_min, int& t_max) {
+  if (rA / Sq == rB / Sq) {
+    t_min = rA % Sq;
+    t_max = rB % Sq;
+  } else {
+    t_min = 0;
+    t_max = Sq - 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
+    float c) {
+  constexpr int KP = D + 8;        // K tile row pitch (elements): 16 B pad
+  constexpr int VP = kBN + 8;      // V^T tile row pitch (elements): 16 B pad
+  constexpr int K_ELEMS = kBN * KP;
+  constexpr int V_ELEMS = D * VP;
+  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
+  constexpr int K_RPI = kThreads / CPR;  // K rows per load instruction
+  constexpr int NK = kBN / K_RPI;        // K loads per thread
+  constexpr int NV = kBN * CPR / kThreads;  // consecutive keys per thread for V (2 or 4)
+  constexpr int V_KG = kBN / NV;         // key groups per tile
+  constexpr int DS = D / 16;             // MFMA k-steps over d for S^T
+  constexpr int DB = D / 32;             // 32-row d blocks of O^T
+  static_assert(NV == 2 || NV == 4, "V staging assumes 2 or 4 keys per thread");
+
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (K_ELEMS + V_ELEMS)];
+
+  const int G = Hq / Hkv;
+  const int rows_total = G * Sq;
+  const int n_mt = (rows_total + kBM - 1) / kBM;
+  const int n_groups = B * Hkv;
+  const TileCoord tc = map_tile(blockIdx.x, n_groups, Hkv, n_mt, G, Sq);
+  const int r0 = tc.mt * kBM;
+  const int q_start = Skv - Sq;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 31;   // query column owned by this lane inside the wave
+  const int hf = l >> 5;   // which half of the key set / d chunk the lane holds
+
+  const size_t head0 = (size_t)tc.b * Hq + (size_t)tc.kvh * G;   // first query head of group
+  const bf16* qg = q + head0 * Sq * D;
+  const size_t kvoff = ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
+  const bf16* kg = k + kvoff;
+  const bf16* vg = v + kvoff;
+
+  // This lane's query row and its global position.
+  const int row = r0 + 32 * w + lr;
+  const bool row_ok = row < rows_total;
+  const int pos = q_start + (row_ok ? row % Sq : 0);
+
+  // Causal extents: loop bound for the workgroup, mask-free bound per wave.
+  int n_tiles = (Skv + kBN - 1) / kBN;
+  int wave_tmin = 0x3fffffff;
+  if (CAUSAL) {
+    int tmin, tmax;
+    row_range_positions(r0, min(r0 + kBM - 1, rows_total - 1), Sq, tmin, tmax);
+    n_tiles = min(n_tiles, (q_start + tmax) / kBN + 1);
+    const int wA = r0 + 32 * w, wB = min(r0 + 32 * w + 31, rows_total - 1);
+    if (wA <= wB) {
+      int a, bb;
+      row_range_positions(wA, wB, Sq, a, bb);
+      wave_tmin = a;
+    }
+  }
+
+  // Q^T B operand: lane holds Q[row][16 s + 8 hf .. +7] for s = 0 .. DS-1.
+  bf16x8 qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row_ok) x = ld16(qg + (size_t)row * D + 16 * s + 8 * hf);
+    qf[s] = as_bf16x8(x);
+  }
+
+  // Staging registers for one K/V tile.
+  u32x4 kst[NK];
+  u32x4 vst[NV];
+  const int k_c = tid % CPR, k_rg = tid / CPR;
+  const int v_kg = tid % V_KG, v_c = tid / V_KG;
+
+  auto load_tile = [&](int kt) {
+    const int key0 = kt * kBN;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int key = key0 + k_rg + K_RPI * i;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < Skv) x = ld16(kg + (size_t)key * D + 8 * k_c);
+      kst[i] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int key = key0 + NV * v_kg + i;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < Skv) x = ld16(vg + (size_t)key * D + 8 * v_c);
+      vst[i] = x;
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
+    bf16* Vs = Ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) st16(Ks + (k_rg + K_RPI * i) * KP + 8 * k_c, kst[i]);
+    // Transposed V: row d = 8 v_c + e holds the NV keys of this thread.
+    const int p0 = vt_pos(NV * v_kg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16* dst = Vs + (8 * v_c + e) * VP + p0;
+      const int dw = e >> 1;
+      if constexpr (NV == 4) {
+        uint32_t a, bq;
+        if (e & 1) {
+          a = pack_hi(vst[0][dw], vst[1][dw]);
+          bq = pack_hi(vst[2][dw], vst[3][dw]);
+        } else {
+          a = pack_lo(vst[0][dw], vst[1][dw]);
+          bq = pack_lo(vst[2][dw], vst[3][dw]);
+        }
+        u32x2 pr = {a, bq};
+        *reinterpret_cast<u32x2*>(dst) = pr;
+      } else {
+        const uint32_t a = (e & 1) ? pack_hi(vst[0][dw], vst[1][dw]) : pack_lo(vst[0][dw], vst[1][dw]);
+        *reinterpret_cast<uint32_t*>(dst) = a;
+      }
+    }
+  };
+
+  // Running state (per lane = per query row, partial over this lane's keys for l).
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < n_tiles) load_tile(kt + 1);
+
+    const bf16* Ks = smem + cur * (K_ELEMS + V_ELEMS);
+    const bf16* Vs = Ks + K_ELEMS;
+
+    // S^T = K Q^T for the two 32-key blocks of the tile.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + lr) * KP + 16 * s + 8 * hf);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+      }
+    }
+
+    // Boundary mask (tail of the key range, causal diagonal): select to -inf.
+    const int key_end = kt * kBN + kBN - 1;
+    const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = (key < Skv) && (!CAUSAL || key <= pos);
+          sacc[kb][r] = vis ? sacc[kb][r] : kNegInf;
+        }
+    }
+
+    // Online softmax in base 2 (c = scale * log2 e > 0).
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float corr = exp2_hw(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
+        sacc[kb][r] = p;
+        psum += p;
+      }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[i][j] *= corr;
+
+    // O^T += V^T P^T; P^T operand = 8 consecutive S^T accumulators, rounded to bf16.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int r8 = 8 * cc;
+        const bf16x8 pf = to_bf16x8(sacc[kb][r8 + 0], sacc[kb][r8 + 1], sacc[kb][r8 + 2], sacc[kb][r8 + 3],
+                                    sacc[kb][r8 + 4], sacc[kb][r8 + 5], sacc[kb][r8 + 6], sacc[kb][r8 + 7]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + (32 * db + lr) * VP + 32 * kb + 16 * cc + 8 * hf);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (kt + 1 < n_tiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2.
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    bf16* orow = o + (head0 * Sq + row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hf;
+        const uint32_t lo = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 0] * inv)),
+                                    __builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 1] * inv)));
+        const uint32_t hi = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 2] * inv)),
+                                    __builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 3] * inv)));
+        u32x2 pr = {lo, hi};
+        *reinterpret_cast<u32x2*>(orow + d0) = pr;
+      }
+    if (lse != nullptr && hf == 0)
+      lse[head0 * Sq + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel
+// ---------------------------------------------------------------------------
+constexpr int kBN32 = 32;   // keys per KV tile (fp32 path)
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
+    float c) {
+  constexpr int KP = D + 1;       // odd pitch: the 32 rows of a K read hit 32 banks
+  constexpr int VP = D + 4;
+  constexpr int CPR = D / 4;      // 16-byte chunks per row
+  constexpr int RPI = kThreads / CPR;
+  constexpr int NL = kBN32 / RPI; // loads per thread per tensor
+  constexpr int DB = D / 32;
+  constexpr int DS = D / 2;
+
+  __shared__ __attribute__((aligned(16))) float Ks[kBN32 * KP];
+  __shared__ __attribute__((aligned(16))) float Vs[kBN32 * VP];
+
+  const int G = Hq / Hkv;
+  const int rows_total = G * Sq;
+  const int n_mt = (rows_total + kBM - 1) / kBM;
+  const TileCoord tc = map_tile(blockIdx.x, B * Hkv, Hkv, n_mt, G, Sq);
+  const int r0 = tc.mt * kBM;
+  const int q_start = Skv - Sq;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, lr = l & 31, hf = l >> 5;
+  const size_t head0 = (size_t)tc.b * Hq + (size_t)tc.kvh * G;
+  const float* qg = q + head0 * Sq * D;
+  const size_t kvoff = ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
+  const float* kg = k + kvoff;
+  const float* vg = v + kvoff;
+
+  const int row = r0 + 32 * w + lr;
+  const bool row_ok = row < rows_total;
+  const int pos = q_start + (row_ok ? row % Sq : 0);
+
+  int n_tiles = (Skv + kBN32 - 1) / kBN32;
+  int wave_tmin = 0x3fffffff;
+  if (CAUSAL) {
+    int tmin, tmax;
+    row_range_positions(r0, min(r0 + kBM - 1, rows_total - 1), Sq, tmin, tmax);
+    n_tiles = min(n_tiles, (q_start + tmax) / kBN32 + 1);
+    const int wA = r0 + 32 * w, wB = min(r0 + 32 * w + 31, rows_total - 1);
+    if (wA <= wB) {
+      int a, bb;
+      row_range_positions(wA, wB, Sq, a, bb);
+      wave_tmin = a;
+    }
+  }
+
+  float qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) qf[s] = row_ok ? qg[(size_t)row * D + 2 * s + hf] : 0.f;
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
+
+  const int ch = tid % CPR, rg = tid / CPR;
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int key0 = kt * kBN32;
+    u32x4 kx[NL], vx[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int key = key0 + rg + RPI * i;
+      u32x4 a = {0u, 0u, 0u, 0u}, b2 = {0u, 0u, 0u, 0u};
+      if (key < Skv) {
+        a = ld16(kg + (size_t)key * D + 4 * ch);
+        b2 = ld16(vg + (size_t)key * D + 4 * ch);
+      }
+      kx[i] = a;
+      vx[i] = b2;
+    }
+    __syncthreads();   // previous tile fully consumed
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      // Bit-cast copies of the elements: clang lowers a bit-cast of a vector
+      // element lvalue as a read of element 0.
+      float* kd = Ks + (rg + RPI * i) * KP + 4 * ch;
+      const f32x4 kf = __builtin_bit_cast(f32x4, kx[i]);
+      kd[0] = kf[0];
+      kd[1] = kf[1];
+      kd[2] = kf[2];
+      kd[3] = kf[3];
+      st16(Vs + (rg + RPI * i) * VP + 4 * ch, vx[i]);
+    }
+    __syncthreads();
+
+    f32x16 sacc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[lr * KP + 2 * s + hf], qf[s], sacc, 0, 0, 0);
+
+    const int key_end = key0 + kBN32 - 1;
+    if ((key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const bool vis = (key < Skv) && (!CAUSAL || key <= pos);
+        sacc[r] = vis ? sacc[r] : kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float corr = exp2_hw(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_hw(__builtin_fmaf(sacc[r], c, -m_use));
+      sacc[r] = p;
+      psum += p;
+    }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[i][j] *= corr;
+
+    // O^T += V^T P^T, two keys per step: k-slot hf of step st = 4 q + s' is
+    // key 8 q + 4 hf + s', i.e. this lane's accumulator st.
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int key = 8 * (st >> 2) + 4 * hf + (st & 3);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VP + 32 * db + lr], sacc[st], oacc[db], 0, 0, 0);
+    }
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    float* orow = o + (head0 * Sq + row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hf;
+        f32x4 val = {oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                     oacc[db][4 * q4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + d0) = val;
+      }
+    if (lse != nullptr && hf == 0)
+      lse[head0 * Sq + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const long long n_mt = ((long long)G * a.Sq + kBM - 1) / kBM;
+  const long long grid = n_mt * (long long)a.B * a.Hkv;
+  const float c = a.scale * kLog2e;
+  const dim3 g((unsigned)grid), blk(kThreads);
+#define SA_LAUNCH_BF16(DD, CC)                                                                      \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC>), g, blk, 0, stream, (const bf16*)a.q,          \
+                     (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, \
+                     a.Skv, c)
+#define SA_LAUNCH_F32(DD, CC)                                                                         \
+  hipLaunchKernelGGL((prefill_f32_kernel<DD, CC>), g, blk, 0, stream, (const float*)a.q,            \
+                     (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, \
+                     a.Skv, c)
+  if (a.bf16) {
+    if (a.d == 128) {
+      if (a.causal) SA_LAUNCH_BF16(128, true); else SA_LAUNCH_BF16(128, false);
+    } else {
+      if (a.causal) SA_LAUNCH_BF16(64, true); else SA_LAUNCH_BF16(64, false);
+    }
+  } else {
+    if (a.d == 128) {
+      if (a.causal) SA_LAUNCH_F32(128, true); else SA_LAUNCH_F32(128, false);
+    } else {
+      if (a.causal) SA_LAUNCH_F32(64, true); else SA_LAUNCH_F32(64, false);
+    }
+  }
+#undef SA_LAUNCH_BF16
+#undef SA_LAUNCH_F32
+  return hipGetLastError();
+}
+
+}  // namespace sa

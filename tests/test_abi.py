@@ -1,0 +1,120 @@
+"""The C ABI library on the CPU: it loads, exports every function the header
+declares, and rejects invalid arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import streaming_attention_amd as sa
+from streaming_attention_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN = 0, 1, 2, 3, 4
+BF16, F32 = 1, 0
+P = 0x10000          # a 16-byte aligned non-null address; never dereferenced here
+MIS = 0x10008        # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("attn_prefill", "attn_decode_splitkv", "attn_combine_lse", "attn_status_string"):
+        assert n in names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = sa.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in attn.h but not exported"
+    assert set(_binding.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings():
+    lib = sa.lib()
+    for code in range(6):
+        s = lib.attn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.attn_status_string(99).decode() == "unknown status"
+
+
+def prefill(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, Sq=16, Skv=32, d=128, dtype=BF16, causal=1,
+            scale=0.088, stream=None):
+    return sa.lib().attn_prefill(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, dtype, causal, scale, stream)
+
+
+def decode(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=100, d=128, max_splits=8,
+           dtype=BF16, scale=0.088, po=P, pl=P, stream=None):
+    return sa.lib().attn_decode_splitkv(q, k, v, kv_len, ns, B, Hq, Hkv, S_cap, d, max_splits, dtype, scale,
+                                        po, pl, stream)
+
+
+def combine(po=P, pl=P, ns=None, B=2, Hq=8, max_splits=8, d=128, o=P, lse=P, dtype=BF16, stream=None):
+    return sa.lib().attn_combine_lse(po, pl, ns, B, Hq, max_splits, d, o, lse, dtype, stream)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL),
+    (dict(Hq=6, Hkv=4), SHAPE), (dict(Hkv=0), SHAPE), (dict(Hq=0), SHAPE), (dict(B=-1), SHAPE),
+    (dict(Sq=-3), SHAPE), (dict(Skv=-1), SHAPE), (dict(Sq=40, Skv=32, causal=1), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(scale=-0.5), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(scale=float("inf")), SHAPE), (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(q=MIS), ALIGN), (dict(k=MIS), ALIGN), (dict(o=MIS), ALIGN), (dict(lse=MIS), ALIGN),
+    (dict(B=0), OK), (dict(Sq=0), OK), (dict(B=0, q=None, o=None), OK),
+    (dict(Hq=64, Hkv=8, Sq=1 << 28, Skv=1 << 28, B=64), SHAPE),
+])
+def test_prefill_host_validation(kw, expect):
+    assert prefill(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), NULL), (dict(po=None), NULL), (dict(pl=None), NULL), (dict(k=None), NULL),
+    (dict(max_splits=0), SHAPE), (dict(max_splits=257), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(B=-2), SHAPE), (dict(S_cap=-1), SHAPE), (dict(scale=0.0), SHAPE),
+    (dict(dtype=F32), UNSUP), (dict(d=80), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+    (dict(q=MIS), ALIGN), (dict(po=MIS), ALIGN), (dict(v=MIS), ALIGN),
+    (dict(B=0), OK), (dict(B=0, q=None, po=None, pl=None), OK),
+])
+def test_decode_host_validation(kw, expect):
+    assert decode(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(po=None), NULL), (dict(pl=None), NULL), (dict(o=None), NULL),
+    (dict(max_splits=0), SHAPE), (dict(max_splits=300), SHAPE), (dict(Hq=0), SHAPE), (dict(B=-1), SHAPE),
+    (dict(d=32), UNSUP), (dict(dtype=9), UNSUP), (dict(o=MIS), ALIGN), (dict(lse=MIS), ALIGN),
+    (dict(B=0), OK),
+])
+def test_combine_host_validation(kw, expect):
+    assert combine(**kw) == expect
+
+
+def test_binding_rejects_cpu_tensors_before_calling_the_library():
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sa.prefill(q, q[:, :1], q[:, :1])
+    with pytest.raises(ValueError):
+        sa.decode_splitkv(q[:, :, :1], q, q)
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    """A missing library is an error, not a silent CPU path."""
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.lib()
+
+
+def test_splits_for_lengths():
+    n = sa.splits_for_lengths(torch.tensor([0, 1, 2048, 2049, 131072, 10 ** 7]))
+    assert n.tolist() == [1, 1, 1, 2, 64, 64]
+    assert n.dtype == torch.int32

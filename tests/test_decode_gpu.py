@@ -1,0 +1,162 @@
+"""attn_decode_splitkv and attn_combine_lse on the GPU against the float64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_attention_amd as sa
+from streaming_attention_amd import workloads as W
+from parity import assert_lse, assert_o, f64, split_bounds
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check_rows(o, lse, q, k, v, lens, scale, seqs, kind="bf16"):
+    """Final decode output of the listed sequences, all heads, vs the oracle."""
+    for b in seqs:
+        n = int(lens[b])
+        O_ref, L_ref = oracle.decode_attention(f64(q[b:b + 1, :, 0]), f64(k[b:b + 1, :, :n]),
+                                               f64(v[b:b + 1, :, :n]), [n], scale)
+        assert_o(o[b, :, 0], O_ref[0], kind, f"O seq {b} len {n}")
+        assert_lse(lse[b], L_ref[0], kind, f"LSE seq {b} len {n}")
+        # relative error over the heads of this sequence
+        num = np.linalg.norm(f64(o[b, :, 0]) - O_ref[0])
+        assert num <= 1e-2 * np.linalg.norm(O_ref[0]), f"rel err seq {b}"
+
+
+def _check_partials(part_o, part_lse, q, k, v, lens, nsplits, scale, seqs, splits=None):
+    """Each split's partial vs the oracle restricted to the split's key range."""
+    for b in seqs:
+        n = int(nsplits[b])
+        bounds = split_bounds(int(lens[b]), n)
+        which = range(n) if splits is None else [s for s in splits if s < n]
+        for s in which:
+            lo, hi = bounds[s]
+            L_ref, O_ref = oracle.partial_attention(f64(q[b, :, 0]), f64(k[b, :, lo:hi]),
+                                                    f64(v[b, :, lo:hi]), scale, 0, hi - lo)
+            assert_o(part_o[b, :, s], O_ref, "bf16", f"partial O seq {b} split {s} [{lo},{hi})")
+            assert_lse(part_lse[b, :, s], L_ref, "bf16", f"partial LSE seq {b} split {s}")
+
+
+def test_gqa70b_decode_full_size():
+    """B=4, 64/8 heads, 32768 keys each, 64 splits: every output row and a
+    sample of split partials, in the benchmark's launch shape."""
+    w = W.GQA70B_DECODE
+    q, k, v, lens = W.decode_inputs(w, DEV)
+    part_o, part_lse = sa.decode_splitkv(q, k, v, None, None, max_splits=w.splits, scale=w.scale)
+    o, lse = sa.combine_lse(part_o, part_lse, None, torch.bfloat16)
+    torch.cuda.synchronize()
+    _check_rows(o, lse, q, k, v, lens, w.scale, range(w.B))
+    ns = [w.splits] * w.B
+    _check_partials(part_o, part_lse, q, k, v, lens, ns, w.scale, [0, 3], splits=[0, 1, 31, 63])
+
+
+def test_ragged_decode_full_size_nan_padding():
+    """B=16, lengths uniform in [1024, 131072] from the seed, split count per
+    length, cache slots past each length filled with NaN."""
+    w = W.RAGGED_DECODE
+    q, k, v, lens = W.decode_inputs(w, DEV)
+    ns = sa.splits_for_lengths(lens)
+    o, lse = sa.decode(q, k, v, lens.to(DEV), ns.to(DEV), max_splits=64, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    order = np.argsort(lens.numpy())
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[7]), 3})
+    _check_rows(o, lse, q, k, v, lens, w.scale, seqs)
+
+
+SMALL = [
+    # B, Hq, Hkv, S_cap, d, lens, nsplits, max_splits
+    (3, 8, 1, 700, 128, [700, 1, 333], [4, 1, 3], 4),
+    (2, 16, 2, 1000, 64, [1000, 64], [7, 7], 8),
+    (4, 4, 4, 300, 128, [0, 5, 299, 300], [2, 3, 1, 5], 5),
+    (2, 32, 2, 129, 128, [129, 128], [256, 3], 256),
+    (1, 64, 8, 4096, 128, [4095], [64], 64),
+    (2, 2, 2, 97, 64, [97, 96], [1, 2], 2),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S_cap,d,lens,nsplits,max_splits", SMALL)
+def test_small_decode_with_partials(B, Hq, Hkv, S_cap, d, lens, nsplits, max_splits):
+    g = torch.Generator(device=DEV).manual_seed(77 + S_cap + d)
+    q = torch.randn((B, Hq, 1, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    for b, n in enumerate(lens):       # poison everything past each length
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    nt = torch.tensor(nsplits, dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(d)
+    part_o, part_lse = sa.decode_splitkv(q, k, v, lt, nt, max_splits=max_splits, scale=scale)
+    o, lse = sa.combine_lse(part_o, part_lse, nt, torch.bfloat16)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            assert (o[b].float() == 0).all() and torch.isneginf(lse[b]).all()
+            continue
+        O_ref, L_ref = oracle.decode_attention(f64(q[b:b + 1, :, 0]), f64(k[b:b + 1, :, :n]),
+                                               f64(v[b:b + 1, :, :n]), [n], scale)
+        assert_o(o[b, :, 0], O_ref[0], "bf16")
+        assert_lse(lse[b], L_ref[0], "bf16")
+    _check_partials(part_o, part_lse, q, k, v, lens, nsplits, scale, range(B))
+
+
+def test_default_lengths_and_splits():
+    """kv_len = NULL means S_cap keys; num_splits = NULL means max_splits."""
+    B, Hq, Hkv, S, d = 2, 8, 1, 517, 128
+    q = torch.randn(B, Hq, 1, d, device=DEV).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, S, d, device=DEV).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, S, d, device=DEV).to(torch.bfloat16)
+    o, lse = sa.decode(q, k, v, max_splits=6)
+    torch.cuda.synchronize()
+    _check_rows(o, lse, q, k, v, [S] * B, 1 / math.sqrt(d), range(B))
+
+
+def test_combine_fp32_output_and_random_partials():
+    """The combine kernel alone on arbitrary partials (including -inf entries)
+    against the oracle's log-sum-exp merge; fp32 output at 1e-4."""
+    rng = np.random.default_rng(3)
+    B, Hq, S, d = 3, 5, 9, 64
+    lse_p = rng.normal(0.0, 3.0, (B, Hq, S))
+    lse_p[0, 0, :4] = -np.inf
+    lse_p[2, :, :] = -np.inf              # a sequence with nothing to attend
+    o_p = rng.standard_normal((B, Hq, S, d))
+    po = torch.tensor(o_p, dtype=torch.float32, device=DEV)
+    pl = torch.tensor(lse_p, dtype=torch.float32, device=DEV)
+    ns = torch.tensor([9, 4, 9], dtype=torch.int32, device=DEV)
+    o, lse = sa.combine_lse(po, pl, ns, torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = int(ns[b])
+        L_ref, O_ref = oracle.merge_partials(np.moveaxis(f64(pl[b, :, :n]), 1, 0),
+                                             np.moveaxis(f64(po[b, :, :n]), 1, 0))
+        assert_o(o[b, :, 0], O_ref, "f32")
+        assert_lse(lse[b], L_ref, "f32")
+
+
+def test_decode_matches_last_row_of_prefill_oracle():
+    """Decode over len keys == the last row of a causal prefill over them."""
+    S, d = 1500, 128
+    q = torch.randn(1, 8, S, d, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 1, S, d, device=DEV).to(torch.bfloat16)
+    v = torch.randn(1, 1, S, d, device=DEV).to(torch.bfloat16)
+    o, lse = sa.decode(q[:, :, -1:].contiguous(), k, v, max_splits=7)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_rows(f64(q[:, :8]), f64(k), f64(v), 1 / math.sqrt(d), True, 0, 0, [S - 1])
+    assert_o(o[0, 0, 0], O_ref[0], "bf16")
+    assert_lse(lse[0, 0], L_ref[0], "bf16")
+
+
+def test_decode_repeat_is_bitwise():
+    w = W.GQA70B_DECODE
+    q, k, v, _ = W.decode_inputs(w, DEV, B=1, S_cap=8192)
+    o1, l1 = sa.decode(q, k, v, max_splits=16)
+    o2, l2 = sa.decode(q, k, v, max_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

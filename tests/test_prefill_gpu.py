@@ -1,0 +1,213 @@
+"""attn_prefill on the GPU against the float64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_attention_amd as sa
+from streaming_attention_amd import workloads as W
+from parity import assert_lse, assert_o, assert_rel_fro, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _kind(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+def run_and_check(q, k, v, causal, scale=None, rel_fro=True):
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = sa.prefill(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(f64(q), f64(k), f64(v), scale, causal)
+    kind = _kind(q)
+    assert_o(o, O_ref, kind)
+    assert_lse(lse, L_ref, kind)
+    if kind == "bf16" and rel_fro:
+        assert_rel_fro(o, O_ref)
+    return o, lse
+
+
+def test_single_head_f32_full():
+    """fp32, B=1, H=1, S=128, d=64, non-causal: the whole output at 1e-4."""
+    w = W.SINGLE_HEAD_F32
+    q, k, v = W.prefill_inputs(w, DEV)
+    run_and_check(q, k, v, w.causal, w.scale)
+
+
+def test_mha_causal_prefill_full():
+    """bf16, B=2, H=16, S=1024, d=64, causal: the whole output."""
+    w = W.MHA_CAUSAL
+    q, k, v = W.prefill_inputs(w, DEV)
+    run_and_check(q, k, v, w.causal, w.scale)
+
+
+# Small shapes that span several tiles, ragged tails, GQA rows of two heads in
+# one 128-row tile, d = 64 and 128, causal on and off, bf16 and fp32.
+SMALL = [
+    # B, Hq, Hkv, Sq, Skv, d, causal, dtype
+    (1, 8, 1, 200, 333, 128, False, torch.bfloat16),
+    (2, 4, 2, 77, 300, 64, True, torch.bfloat16),
+    (1, 16, 2, 130, 130, 128, True, torch.bfloat16),
+    (1, 8, 8, 1, 257, 128, True, torch.bfloat16),
+    (2, 6, 3, 96, 96, 64, False, torch.bfloat16),
+    (1, 2, 1, 65, 65, 128, True, torch.float32),
+    (1, 4, 2, 100, 190, 64, True, torch.float32),
+    (2, 2, 2, 33, 31, 128, False, torch.float32),
+    (1, 1, 1, 1, 1, 64, True, torch.bfloat16),
+    (1, 32, 8, 48, 1000, 128, True, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal,dtype", SMALL)
+def test_small_shapes(B, Hq, Hkv, Sq, Skv, d, causal, dtype):
+    g = torch.Generator(device=DEV).manual_seed(1000 + Sq + Skv + d)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV).to(dtype)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(dtype)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(dtype)
+    run_and_check(q, k, v, causal)
+
+
+def _sampled_rows_check(w, n_rows_per_head=6, heads=(0, 7, 8, 31, 63)):
+    q, k, v = W.prefill_inputs(w, DEV)
+    o, lse = sa.prefill(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(w.seed)
+    worst_o = worst_l = 0.0
+    kv_cache = {}
+    for h in heads:
+        kvh = h // (w.Hq // w.Hkv)
+        if kvh not in kv_cache:
+            kv_cache[kvh] = (f64(k[:, kvh:kvh + 1]), f64(v[:, kvh:kvh + 1]))
+        kh, vh = kv_cache[kvh]
+        rows = sorted(set([0, w.Sq - 1] + rng.integers(0, w.Sq, n_rows_per_head).tolist()))
+        qh = f64(q[:, h:h + 1])
+        O_ref, L_ref = oracle.attention_rows(qh, kh, vh, w.scale, w.causal, 0, 0, rows)
+        worst_o = max(worst_o, assert_o(o[0, h, rows], O_ref, "bf16", f"O head {h}"))
+        worst_l = max(worst_l, assert_lse(lse[0, h, rows], L_ref, "bf16", f"LSE head {h}"))
+        # relative error of the sampled rows as one block
+        num = np.linalg.norm(f64(o[0, h, rows]) - O_ref)
+        assert num <= 1e-2 * np.linalg.norm(O_ref), f"rel err head {h}"
+    return worst_o, worst_l
+
+
+def test_gqa70b_prefill_full_size_sampled_rows():
+    """B=1, 64/8 heads, S=8192, d=128, causal, in the benchmark's launch shape."""
+    _sampled_rows_check(W.GQA70B_PREFILL)
+
+
+def test_chunked_prefill_full_size_sampled_rows():
+    """512 new queries over a 65536-token prefix (bottom-right causal)."""
+    _sampled_rows_check(W.CHUNKED_PREFILL, n_rows_per_head=4)
+
+
+def test_skv_zero_noncausal_gives_zero_and_neg_inf():
+    q = torch.randn(1, 2, 5, 64, device=DEV).to(torch.bfloat16)
+    k = torch.empty(1, 1, 0, 64, device=DEV, dtype=torch.bfloat16)
+    o, lse = sa.prefill(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert (o.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_empty_query_block_is_a_noop():
+    q = torch.empty(1, 2, 0, 128, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn(1, 1, 9, 128, device=DEV).to(torch.bfloat16)
+    o, lse = sa.prefill(q, k, k, causal=True)
+    assert o.shape == (1, 2, 0, 128) and lse.shape == (1, 2, 0)
+
+
+def test_zero_k_gives_running_mean_of_v():
+    """K = 0: uniform weights, O_t = mean of visible V rows, LSE_t = ln n_t."""
+    Sq = Skv = 300
+    q = torch.randn(1, 4, Sq, 128, device=DEV).to(torch.bfloat16)
+    k = torch.zeros(1, 2, Skv, 128, device=DEV, dtype=torch.bfloat16)
+    v = torch.randn(1, 2, Skv, 128, device=DEV).to(torch.bfloat16)
+    o, lse = sa.prefill(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    vv = f64(v)
+    n = np.arange(1, Sq + 1)
+    mean = np.cumsum(vv, axis=2) / n[None, None, :, None]
+    ref = np.repeat(mean, 2, axis=1)
+    assert_o(o, ref, "bf16")
+    assert_lse(lse, np.broadcast_to(np.log(n), (1, 4, Sq)), "bf16")
+
+
+def test_one_hot_scores_select_one_value_row():
+    """K rows are unit vectors; query t puts 1024 on coordinate pi(t) <= t, so
+    softmax saturates on key pi(t): O_t = V_pi(t), LSE_t = 1024 * scale (+ tiny)."""
+    S, d = 128, 128
+    scale = 1.0 / math.sqrt(d)
+    k = torch.eye(S, d, device=DEV).to(torch.bfloat16)[None, None]
+    rng = np.random.default_rng(5)
+    pick = [int(rng.integers(0, t + 1)) for t in range(S)]
+    q = torch.zeros(1, 1, S, d, device=DEV)
+    for t, p in enumerate(pick):
+        q[0, 0, t, p] = 1024.0
+    q = q.to(torch.bfloat16)
+    v = torch.randn(1, 1, S, d, device=DEV).to(torch.bfloat16)
+    o, lse = sa.prefill(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ref = f64(v)[0, 0, pick]
+    assert_o(o[0, 0], ref, "bf16")
+    a = 1024.0 * scale
+    lse_ref = [a + math.log1p(t * math.exp(-a)) for t in range(S)]
+    assert_lse(lse[0, 0], lse_ref, "bf16")
+
+
+def test_scale_folding_is_bitwise():
+    """(2Q, scale/2) and (Q, scale) give bitwise-identical outputs: doubling a
+    bf16 value and halving the fp32 scale are both exact."""
+    q = torch.randn(1, 8, 256, 128, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 2, 256, 128, device=DEV).to(torch.bfloat16)
+    v = torch.randn(1, 2, 256, 128, device=DEV).to(torch.bfloat16)
+    o1, l1 = sa.prefill(q, k, v, causal=True, scale=0.125)
+    o2, l2 = sa.prefill(q * 2, k, v, causal=True, scale=0.0625)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = W.MHA_CAUSAL
+    q, k, v = W.prefill_inputs(w, DEV)
+    o1, l1 = sa.prefill(q, k, v, causal=True)
+    o2, l2 = sa.prefill(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_and_repeated_mha_both_match_the_oracle():
+    """The same attention as GQA (8 query heads per KV head) and as MHA on
+    repeat-interleaved K/V: both launches against the one GQA oracle result."""
+    q = torch.randn(1, 16, 200, 128, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 2, 200, 128, device=DEV).to(torch.bfloat16)
+    v = torch.randn(1, 2, 200, 128, device=DEV).to(torch.bfloat16)
+    O_ref, L_ref = oracle.attention(f64(q), f64(k), f64(v), 1 / math.sqrt(128), True)
+    o1, l1 = sa.prefill(q, k, v, causal=True)
+    kr = k.repeat_interleave(8, dim=1).contiguous()
+    vr = v.repeat_interleave(8, dim=1).contiguous()
+    o2, l2 = sa.prefill(q, kr, vr, causal=True)
+    torch.cuda.synchronize()
+    for o, l in ((o1, l1), (o2, l2)):
+        assert_o(o, O_ref, "bf16")
+        assert_lse(l, L_ref, "bf16")
+
+
+def test_nan_after_the_last_key_row_is_never_read():
+    """Keys past Skv are never read: K and V are views at the front of larger
+    NaN-filled buffers, so the bytes right after their last row are NaN."""
+    Skv, shape = 100, (1, 2, 100, 128)
+    n = 1 * 2 * Skv * 128
+    kbuf = torch.full((n + 64 * 128,), float("nan"), device=DEV, dtype=torch.bfloat16)
+    vbuf = torch.full_like(kbuf, float("nan"))
+    k = kbuf[:n].view(shape)
+    v = vbuf[:n].view(shape)
+    k.copy_(torch.randn(shape, device=DEV).to(torch.bfloat16))
+    v.copy_(torch.randn(shape, device=DEV).to(torch.bfloat16))
+    q = torch.randn(1, 4, 70, 128, device=DEV).to(torch.bfloat16)
+    run_and_check(q, k, v, causal=True)
