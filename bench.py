@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="run only one half of the step (for per-kernel profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -114,14 +116,19 @@ def main():
     n_ev = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
 
+    do_pf = args.only in ("all", "prefill")
+    do_dc = args.only in ("all", "decode")
+
     def step(i=None):
         if i is not None:
             ev[i][0].record(stream)
-        sa.prefill(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
+        if do_pf:
+            sa.prefill(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
         if i is not None:
             ev[i][1].record(stream)
-        sa.decode(qd, kc, vc, None, None, max_splits=wd.splits, scale=wd.scale,
-                  part_o=part_o, part_lse=part_lse, out=od, lse=lsed)
+        if do_dc:
+            sa.decode(qd, kc, vc, None, None, max_splits=wd.splits, scale=wd.scale,
+                      part_o=part_o, part_lse=part_lse, out=od, lse=lsed)
         if i is not None:
             ev[i][2].record(stream)
 
@@ -139,9 +146,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     pf_flops = wp.flops()
-    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12 if do_pf else 0.0
     kv_bytes = W.decode_kv_bytes(lens, wd.Hkv, wd.d)
-    dc_gbs = kv_bytes / (dc_ms * 1e-3) / 1e9
+    dc_gbs = kv_bytes / (dc_ms * 1e-3) / 1e9 if do_dc else 0.0
 
     result = {
         "metric": METRIC,

@@ -90,7 +90,7 @@ int attn_combine_lse(const float* part_o, const float* part_lse, const int32_t* 
   if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
-  if (((long long)B * Hq + 3) / 4 > kMaxGrid) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
   if (B == 0) return ATTN_OK;
   if (part_o == nullptr || part_lse == nullptr || o == nullptr) return ATTN_ERR_NULL;
   if (!aligned16(part_o) || !aligned16(part_lse) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;

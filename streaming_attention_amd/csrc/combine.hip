@@ -5,18 +5,24 @@
 // O = O_a e^{m_a - m} + O_b e^{m_b - m}, normalised once at the end.  With the
 // partials carried as (lse_s, O_s / l_s) this is M = max_s lse_s,
 // w_s = e^{lse_s - M}, O = sum w_s O_s / sum w_s, LSE = M + ln sum w_s.  The
-// merge is associative and commutative, so one pass over all splits of a row
-// is a valid merge order.
+// merge is associative and commutative, so any grouping of the splits is a
+// valid merge order.
 //
-// MI355X mapping: one wave per (sequence, query head) row, each lane owning
-// D / 64 consecutive output elements; the splits are read in order with
-// coalesced 256/512-byte wave loads.  The split-lse maximum is a wave
-// reduction.  This kernel moves ~1.6% of the decode KV bytes.
+// MI355X mapping: one workgroup (4 waves) per (sequence, query head) row.  The
+// row's split maximum M is a workgroup reduction over part_lse.  Wave w then
+// accumulates splits w, w + 4, ... with all its partial-row loads issued before
+// they are consumed (the loop is unrolled), each lane owning D / 64 output
+// elements, and the four wave sums are added through LDS.  The kernel is
+// latency-bound (a few MB in total), so the point is to keep many independent
+// loads in flight, not to stream.
 #include "common.h"
 #include "launch.h"
 
 namespace sa {
 namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 8;
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restrict__ part_o,
@@ -25,18 +31,24 @@ __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restric
                                                           int Hq, int max_splits, void* __restrict__ o,
                                                           float* __restrict__ lse) {
   constexpr int PER = D / 64;   // output elements per lane
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (row >= B * Hq) return;
+  __shared__ float red[kWaves];
+  __shared__ float acc_s[kWaves][D];
+  __shared__ float wsum_s[kWaves];
+
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int b = row / Hq;
   int n = num_splits ? num_splits[b] : max_splits;
   n = n < 1 ? 1 : (n > max_splits ? max_splits : n);
 
+  // M = max over the row's split lse values (n <= 256 = one value per thread).
   const float* L = part_lse + (size_t)row * max_splits;
-  float M = kNegInf;
-  for (int i = l; i < n; i += 64) M = fmaxf(M, L[i]);
+  float M = tid < n ? L[tid] : kNegInf;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (l == 0) red[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   float acc[PER];
 #pragma unroll
@@ -44,31 +56,50 @@ __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restric
   float wsum = 0.f;
   if (M != kNegInf) {
     const float* Op = part_o + (size_t)row * max_splits * D + PER * l;
-    for (int s = 0; s < n; ++s) {
-      const float wgt = exp2_hw((L[s] - M) * kLog2e);
-      wsum += wgt;
+    for (int s0 = w; s0 < n; s0 += kWaves * kUnroll) {
+      float lv[kUnroll];
+      float ov[kUnroll][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += wgt * Op[(size_t)s * D + i];
+      for (int u = 0; u < kUnroll; ++u) {
+        const int s = s0 + kWaves * u;
+        lv[u] = s < n ? L[s] : kNegInf;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ov[u][i] = s < n ? Op[(size_t)s * D + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float wgt = exp2_hw((lv[u] - M) * kLog2e);   // exp2(-inf) = 0 for empty splits
+        wsum += wgt;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += wgt * ov[u][i];
+      }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  if (OUT_BF16) {
-    bf16* out = reinterpret_cast<bf16*>(o) + (size_t)row * D + PER * l;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[i] = (bf16)(acc[i] * inv);
-  } else {
-    float* out = reinterpret_cast<float*>(o) + (size_t)row * D + PER * l;
+  for (int i = 0; i < PER; ++i) acc_s[w][PER * l + i] = acc[i];
+  if (l == 0) wsum_s[w] = wsum;
+  __syncthreads();
+  if (w != 0) return;
+
+  const float ws = wsum_s[0] + wsum_s[1] + wsum_s[2] + wsum_s[3];
+  const float inv = ws > 0.f ? 1.f / ws : 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[i] = acc[i] * inv;
+  for (int i = 0; i < PER; ++i) {
+    const int d = PER * l + i;
+    const float val = (acc_s[0][d] + acc_s[1][d] + acc_s[2][d] + acc_s[3][d]) * inv;
+    if (OUT_BF16)
+      reinterpret_cast<bf16*>(o)[(size_t)row * D + d] = (bf16)val;
+    else
+      reinterpret_cast<float*>(o)[(size_t)row * D + d] = val;
   }
-  if (lse != nullptr && l == 0) lse[row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+  if (lse != nullptr && l == 0) lse[row] = ws > 0.f ? M + __logf(ws) : kNegInf;
 }
 
 }  // namespace
 
 hipError_t launch_combine_lse(const CombineArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.Hq;
-  const dim3 g((unsigned)((rows + 3) / 4)), blk(256);
+  const dim3 g((unsigned)rows), blk(256);
 #define SA_LAUNCH(DD, BF)                                                                                   \
   hipLaunchKernelGGL((combine_lse_kernel<DD, BF>), g, blk, 0, stream, a.part_o, a.part_lse, a.num_splits, a.B, \
                      a.Hq, a.max_splits, a.o, a.lse)

@@ -35,9 +35,58 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   return r;
 }
 
-// Low / high 16-bit halves of two dwords packed into one dword.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// Low / high 16-bit halves of two dwords packed into one dword (one
+// v_perm_b32 each: selector bytes 0-3 pick from the second operand, 4-7 from
+// the first).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Raw buffer resource over [base, base + nbytes): loads at offsets at or past
+// nbytes return zero, so tails need no clamping or predication.  Word 3 selects
+// 32-bit data format, as raw (untyped, stride 0) buffer access requires on gfx9.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+// 16-byte buffer load at byte offset voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// Max of 32 values held in two 16-float accumulators with 3-input max ops.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max_of32(const f32x16& a, const f32x16& b) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[i] = max3f(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[5 + i] = max3f(b[3 * i], b[3 * i + 1], b[3 * i + 2]);
+  t[10] = fmaxf(a[15], b[15]);
+  const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]), u2 = max3f(t[6], t[7], t[8]);
+  return max3f(max3f(u0, u1, u2), t[9], t[10]);
+}
+
+// Pairwise (tree) max / sum of the 32 values of two 16-float accumulators:
+// depth 5 instead of a 32-long dependent chain.
+__device__ __forceinline__ float max_tree32(const f32x16& a, const f32x16& b) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = fmaxf(a[i], b[i]);
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+  return t[0];
+}
+__device__ __forceinline__ float sum_tree32(const f32x16& a, const f32x16& b) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = a[i] + b[i];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = t[i] + t[i + w];
+  return t[0];
+}
 
 // Lane exchange across the two 32-lane halves of a wave (lane l <-> l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }

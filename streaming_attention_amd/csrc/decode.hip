@@ -110,26 +110,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
     u32x4 v[C::NGRP][4];
   };
 
+  // Keys past the split end are read clamped to its last key (finite data,
+  // masked to -inf in the scores, so P = 0 for them); cache slots at or past
+  // kv_len are never touched.  Unconditional loads let the next chunk's loads
+  // stay in flight while the current one is processed.
   auto load_chunk = [&](Regs& R, int key0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = key0 + 16 * kb + j16;
+      const int key = min(key0 + 16 * kb + j16, hi - 1);
 #pragma unroll
-      for (int st = 0; st < C::DS; ++st) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < hi) x = ld16(kg + (size_t)key * D + 32 * st + 8 * qq);
-        R.k[kb][st] = x;
-      }
+      for (int st = 0; st < C::DS; ++st) R.k[kb][st] = ld16(kg + (size_t)key * D + 32 * st + 8 * qq);
     }
 #pragma unroll
     for (int g = 0; g < C::NGRP; ++g) {
       const int kgid = vsub + C::LQ * g;   // 4-key group index 0..7 inside the chunk
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * kgid + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < hi) x = ld16(vg + (size_t)key * D + 8 * vcol);
-        R.v[g][r] = x;
+        const int key = min(key0 + 4 * kgid + r, hi - 1);
+        R.v[g][r] = ld16(vg + (size_t)key * D + 8 * vcol);
       }
     }
   };
@@ -141,12 +139,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nch = (hi - lo + kChunk - 1) / kChunk;
-  Regs cur, nxt;
-  int ci = w;
-  if (ci < nch) load_chunk(cur, lo + ci * kChunk);
-  for (; ci < nch; ci += 4) {
-    if (ci + 4 < nch) load_chunk(nxt, lo + (ci + 4) * kChunk);
+  const int nch = __builtin_amdgcn_readfirstlane((hi - lo + kChunk - 1) / kChunk);
+
+  auto process = [&](const Regs& R, int ci) {
     const int key0 = lo + ci * kChunk;
 
     // S^T for keys key0 + 16 kb + (0..15).
@@ -156,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < C::DS; ++st)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[kb][st]), qf[st], sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[kb][st]), qf[st], sacc[kb], 0, 0, 0);
     }
     if (key0 + kChunk > hi) {
 #pragma unroll
@@ -168,7 +163,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
         }
     }
 
-    // V -> LDS, transposed: row d, key position 8 q + 4 kb + r.
+    // V -> LDS, transposed: row d, key position 8 q + 4 kb + r.  The wave's
+    // previous reads of this region must be complete before it is rewritten.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -180,11 +176,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
         const int dw = e >> 1;
         uint32_t a, bq;
         if (e & 1) {
-          a = pack_hi(cur.v[g][0][dw], cur.v[g][1][dw]);
-          bq = pack_hi(cur.v[g][2][dw], cur.v[g][3][dw]);
+          a = pack_hi(R.v[g][0][dw], R.v[g][1][dw]);
+          bq = pack_hi(R.v[g][2][dw], R.v[g][3][dw]);
         } else {
-          a = pack_lo(cur.v[g][0][dw], cur.v[g][1][dw]);
-          bq = pack_lo(cur.v[g][2][dw], cur.v[g][3][dw]);
+          a = pack_lo(R.v[g][0][dw], R.v[g][1][dw]);
+          bq = pack_lo(R.v[g][2][dw], R.v[g][3][dw]);
         }
         u32x2 pr = {a, bq};
         *reinterpret_cast<u32x2*>(VT + (8 * vcol + e) * C::VTP + p0) = pr;
@@ -224,7 +220,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(VT + (16 * db + j16) * C::VTP + 8 * qq);
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[db], 0, 0, 0);
     }
-    cur = nxt;
+  };
+
+  // Two register buffers in ping-pong, no copies between them, so the next
+  // chunk's loads stay in flight while the current chunk is processed.
+  Regs ra, rb;
+  int ci = w;
+  if (ci < nch) load_chunk(ra, lo + ci * kChunk);
+  if (ci + 4 < nch) load_chunk(rb, lo + (ci + 4) * kChunk);
+  while (ci < nch) {
+    process(ra, ci);
+    if (ci + 8 < nch) load_chunk(ra, lo + (ci + 8) * kChunk);
+    ci += 4;
+    if (ci >= nch) break;
+    process(rb, ci);
+    if (ci + 8 < nch) load_chunk(rb, lo + (ci + 8) * kChunk);
+    ci += 4;
   }
 
   // Row sum over the 4 lanes of the query column.

@@ -46,6 +46,7 @@ namespace {
 constexpr int kBM = 128;   // stacked query rows per workgroup
 constexpr int kBN = 64;    // keys per KV tile (bf16 path)
 constexpr int kThreads = 256;
+constexpr float kRescaleLog2 = 8.f;   // lazy-rescale threshold (log2 units)
 
 // Permutation of a key index inside a 64-key tile for the V^T layout in LDS:
 // swap bits 2 and 3.
@@ -163,13 +164,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   }
 
   // Q^T B operand: lane holds Q[row][16 s + 8 hf .. +7] for s = 0 .. DS-1.
+  // Buffer loads: rows past the group's last stacked row read as zero.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)rows_total * D * 2);
   bf16x8 qf[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row_ok) x = ld16(qg + (size_t)row * D + 16 * s + 8 * hf);
-    qf[s] = as_bf16x8(x);
-  }
+  for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(buf_ld16(rq, (uint32_t)row * D * 2 + 16 * hf + 32 * s, 0));
 
   // Staging registers for one K/V tile.
   u32x4 kst[NK];
@@ -177,22 +176,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int k_c = tid % CPR, k_rg = tid / CPR;
   const int v_kg = tid % V_KG, v_c = tid / V_KG;
 
+  // K/V tiles come in through buffer loads over this (batch, KV head)'s rows:
+  // rows at or past Skv read as zero (their scores are masked to -inf, so P = 0
+  // and the zero V rows contribute nothing).  Per-lane offsets are fixed; the
+  // tile advances through the wave-uniform offset, so the loop spends no VALU
+  // on addresses, and unconditional loads stay in flight across the whole
+  // compute of the current tile.
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (uint32_t)Skv * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (uint32_t)Skv * D * 2);
+  const uint32_t k_voff = (uint32_t)(k_rg * D + 8 * k_c) * 2;
+  const uint32_t v_voff = (uint32_t)(NV * v_kg * D + 8 * v_c) * 2;
   auto load_tile = [&](int kt) {
-    const int key0 = kt * kBN;
+    const uint32_t tile_off = (uint32_t)kt * kBN * D * 2;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int key = key0 + k_rg + K_RPI * i;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < Skv) x = ld16(kg + (size_t)key * D + 8 * k_c);
-      kst[i] = x;
-    }
+    for (int i = 0; i < NK; ++i) kst[i] = buf_ld16(rk, k_voff, tile_off + (uint32_t)(K_RPI * i * D * 2));
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int key = key0 + NV * v_kg + i;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < Skv) x = ld16(vg + (size_t)key * D + 8 * v_c);
-      vst[i] = x;
-    }
+    for (int i = 0; i < NV; ++i) vst[i] = buf_ld16(rv, v_voff + (uint32_t)(i * D * 2), tile_off);
   };
 
   auto store_tile = [&](int buf) {
@@ -233,6 +232,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
 
+  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+  wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
@@ -241,7 +242,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+    // Prefetch the next tile (the last iteration re-reads the last tile into
+    // the idle buffer, which keeps the loads unconditional).
+    load_tile(min(kt + 1, n_tiles - 1));
 
     const bf16* Ks = smem + cur * (K_ELEMS + V_ELEMS);
     const bf16* Vs = Ks + K_ELEMS;
@@ -275,31 +278,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         }
     }
 
-    // Online softmax in base 2 (c = scale * log2 e > 0).
-    float mx = kNegInf;
+    // Online softmax in base 2 (c = scale * log2 e > 0).  The running max used
+    // as the exponent base is only raised when a row's tile max exceeds it by
+    // more than kRescaleLog2 (then O and l are rescaled); otherwise P may reach
+    // 2^kRescaleLog2, which fp32 and bf16 hold exactly enough.  O and l always
+    // share the same base, so O / l is unchanged (the rescale is skipped, not
+    // approximated).
+    const float mx = fmaxf(max_of32(sacc[0], sacc[1]), xor32(max_of32(sacc[0], sacc[1]))) * c;
+    const bool grow = mx > m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float corr = exp2_hw(m_run - m_new);   // 0 when m_run = -inf, 1 when unchanged
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[i][j] *= corr;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float corr = exp2_hw(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
-        sacc[kb][r] = p;
-        psum += p;
-      }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[i][j] *= corr;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
+    l_run += sum_tree32(sacc[0], sacc[1]);
 
     // O^T += V^T P^T; P^T operand = 8 consecutive S^T accumulators, rounded to bf16.
 #pragma unroll
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       }
     }
 
-    if (kt + 1 < n_tiles) store_tile(cur ^ 1);
+    store_tile(cur ^ 1);
     __syncthreads();
   }
 
