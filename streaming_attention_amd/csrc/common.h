@@ -88,7 +88,19 @@ __device__ __forceinline__ float sum_tree32(const f32x16& a, const f32x16& b) {
   return t[0];
 }
 
-// Lane exchange across the two 32-lane halves of a wave (lane l <-> l ^ 32).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one in lane l ^ 32 through v_permlane32_swap (a
+// VALU op; no LDS round trip).  Swapping the upper half of one copy with the
+// lower half of another leaves, in every lane, its own value in one result
+// and its partner's in the other.
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
 
 }  // namespace sa

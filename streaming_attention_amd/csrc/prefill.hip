@@ -47,6 +47,7 @@ constexpr int kBM = 128;   // stacked query rows per workgroup
 constexpr int kBN = 64;    // keys per KV tile (bf16 path)
 constexpr int kThreads = 256;
 constexpr float kRescaleLog2 = 8.f;   // lazy-rescale threshold (log2 units)
+constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
 
 // Permutation of a key index inside a 64-key tile for the V^T layout in LDS:
 // swap bits 2 and 3.
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   constexpr int DB = D / 32;             // 32-row d blocks of O^T
   static_assert(NV == 2 || NV == 4, "V staging assumes 2 or 4 keys per thread");
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (K_ELEMS + V_ELEMS)];
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * K_ELEMS + 2 * V_ELEMS];
 
   const int G = Hq / Hkv;
   const int rows_total = G * Sq;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(buf_ld16(rq, (uint32_t)row * D * 2 + 16 * hf + 32 * s, 0));
 
-  // Staging registers for one K/V tile.
+  // Staging registers for one K tile and one V tile.
   u32x4 kst[NK];
   u32x4 vst[NV];
   const int k_c = tid % CPR, k_rg = tid / CPR;
@@ -180,26 +181,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // rows at or past Skv read as zero (their scores are masked to -inf, so P = 0
   // and the zero V rows contribute nothing).  Per-lane offsets are fixed; the
   // tile advances through the wave-uniform offset, so the loop spends no VALU
-  // on addresses, and unconditional loads stay in flight across the whole
-  // compute of the current tile.
+  // on addresses, and unconditional loads stay in flight across a whole tile.
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (uint32_t)Skv * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (uint32_t)Skv * D * 2);
   const uint32_t k_voff = (uint32_t)(k_rg * D + 8 * k_c) * 2;
   const uint32_t v_voff = (uint32_t)(NV * v_kg * D + 8 * v_c) * 2;
-  auto load_tile = [&](int kt) {
+  auto load_k = [&](int kt) {
     const uint32_t tile_off = (uint32_t)kt * kBN * D * 2;
 #pragma unroll
     for (int i = 0; i < NK; ++i) kst[i] = buf_ld16(rk, k_voff, tile_off + (uint32_t)(K_RPI * i * D * 2));
+  };
+  auto load_v = [&](int kt) {
+    const uint32_t tile_off = (uint32_t)kt * kBN * D * 2;
 #pragma unroll
     for (int i = 0; i < NV; ++i) vst[i] = buf_ld16(rv, v_voff + (uint32_t)(i * D * 2), tile_off);
   };
 
-  auto store_tile = [&](int buf) {
-    bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
-    bf16* Vs = Ks + K_ELEMS;
+  // LDS: a ring of two K tiles [key][d] and a ring of two V^T tiles [d][key'].
+  bf16* const Kring = smem;
+  bf16* const Vring = smem + 2 * K_ELEMS;
+  auto store_k = [&](int buf) {
+    bf16* Ks = Kring + buf * K_ELEMS;
 #pragma unroll
     for (int i = 0; i < NK; ++i) st16(Ks + (k_rg + K_RPI * i) * KP + 8 * k_c, kst[i]);
+  };
+  auto store_v = [&](int buf) {
     // Transposed V: row d = 8 v_c + e holds the NV keys of this thread.
+    bf16* Vs = Vring + buf * V_ELEMS;
     const int p0 = vt_pos(NV * v_kg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -223,6 +231,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
+  // S^T = K Q^T for the two 32-key blocks of the tile in K buffer `buf`.
+  auto scores = [&](int buf, f32x16 (&S)[2]) {
+    const bf16* Ks = Kring + buf * K_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) S[kb][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + lr) * KP + 16 * s + 8 * hf);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[kb], 0, 0, 0);
+      }
+    }
+  };
+
   // Running state (per lane = per query row, partial over this lane's keys for l).
   float m_run = kNegInf;
   float l_run = 0.f;
@@ -232,39 +257,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
 
-  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-  wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int cur = kt & 1;
-    // Prefetch the next tile (the last iteration re-reads the last tile into
-    // the idle buffer, which keeps the loads unconditional).
-    load_tile(min(kt + 1, n_tiles - 1));
-
-    const bf16* Ks = smem + cur * (K_ELEMS + V_ELEMS);
-    const bf16* Vs = Ks + K_ELEMS;
-
-    // S^T = K Q^T for the two 32-key blocks of the tile.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + lr) * KP + 16 * s + 8 * hf);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // Boundary mask (tail of the key range, causal diagonal): select to -inf.
+  // One pipelined step: mask and softmax of tile kt (scores in S), the score
+  // MFMAs of tile kt + 1 (into Snext, from K buffer kbuf_next; after the last
+  // tile they run on an idle buffer and are discarded, which keeps them in the
+  // same basic block as the softmax they interleave with), then
+  // O^T += V^T P^T for tile kt (V^T buffer vbuf).
+  auto step = [&](int kt, f32x16 (&S)[2], f32x16 (&Snext)[2], int kbuf_next, int vbuf) {
+    // P1: boundary mask (tail of the key range, causal diagonal) as a select
+    // to -inf, then the row max and the lazy-rescale decision.
     const int key_end = kt * kBN + kBN - 1;
     const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
     if (need_mask) {
@@ -274,17 +274,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r) {
           const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
           const bool vis = (key < Skv) && (!CAUSAL || key <= pos);
-          sacc[kb][r] = vis ? sacc[kb][r] : kNegInf;
+          S[kb][r] = vis ? S[kb][r] : kNegInf;
         }
     }
-
     // Online softmax in base 2 (c = scale * log2 e > 0).  The running max used
     // as the exponent base is only raised when a row's tile max exceeds it by
     // more than kRescaleLog2 (then O and l are rescaled); otherwise P may reach
     // 2^kRescaleLog2, which fp32 and bf16 hold exactly enough.  O and l always
     // share the same base, so O / l is unchanged (the rescale is skipped, not
     // approximated).
-    const float mx = fmaxf(max_of32(sacc[0], sacc[1]), xor32(max_of32(sacc[0], sacc[1]))) * c;
+    const float mloc = max_of32(S[0], S[1]);
+    const float mx = max_xor32(mloc) * c;
     const bool grow = mx > m_run + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -297,34 +297,89 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       m_run = m_new;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+
+    // P2: next tile's score MFMAs interleaved with this tile's exponentials
+    // and bf16 packing (independent work: the VALU runs while the MFMAs do).
+    scores(kbuf_next, Snext);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
-    l_run += sum_tree32(sacc[0], sacc[1]);
-
-    // O^T += V^T P^T; P^T operand = 8 consecutive S^T accumulators, rounded to bf16.
+      for (int r = 0; r < 16; ++r) S[kb][r] = exp2_hw(__builtin_fmaf(S[kb][r], c, -m_use));
+    bf16x8 pf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int r8 = 8 * cc;
-        const bf16x8 pf = to_bf16x8(sacc[kb][r8 + 0], sacc[kb][r8 + 1], sacc[kb][r8 + 2], sacc[kb][r8 + 3],
-                                    sacc[kb][r8 + 4], sacc[kb][r8 + 5], sacc[kb][r8 + 6], sacc[kb][r8 + 7]);
+        pf[kb][cc] = to_bf16x8(S[kb][r8 + 0], S[kb][r8 + 1], S[kb][r8 + 2], S[kb][r8 + 3],
+                               S[kb][r8 + 4], S[kb][r8 + 5], S[kb][r8 + 6], S[kb][r8 + 7]);
+      }
+    // Schedule: LDS reads run kLdsAhead fragments ahead of their MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
+      if (i + kLdsAhead < 2 * DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
+    }
+
+    // P3: O^T += V^T P^T, interleaved with the row-sum tree.
+    const bf16* Vs = Vring + vbuf * V_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + (32 * db + lr) * VP + 32 * kb + 16 * cc + 8 * hf);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][cc], oacc[db], 0, 0, 0);
         }
-      }
+    l_run += sum_tree32(S[0], S[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU
+      if (i + kLdsAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
     }
+  };
 
-    store_tile(cur ^ 1);
+  // Software pipeline (the pages' "issue the next Q K^T before this tile's
+  // softmax"): K runs one tile ahead of V.  In iteration kt a wave issues the
+  // score MFMAs of tile kt + 1, then the softmax of tile kt (independent VALU
+  // work that executes while those MFMAs run), then the P V MFMAs of tile kt.
+  // K tile kt + 2 and V tile kt + 1 are loaded during the iteration and stored
+  // into the buffers that iteration kt - 1 finished reading; one barrier per
+  // tile orders the rings.
+  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+  wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
+  f32x16 sA[2], sB[2];
+  if (n_tiles > 0) {
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    load_k(1);
+    store_k(1);
     __syncthreads();
+    scores(0, sA);
+    __syncthreads();   // K buffer 0 is rewritten in iteration 0
+  }
+  auto iteration = [&](int kt, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    load_k(kt + 2);    // past the last tile these read zeros, stored into idle buffers
+    load_v(kt + 1);
+    step(kt, Scur, Snext, (kt + 1) & 1, kt & 1);
+    store_k(kt & 1);
+    store_v((kt + 1) & 1);
+    __syncthreads();
+  };
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    iteration(kt, sA, sB);
+    if (kt + 1 < n_tiles) iteration(kt + 1, sB, sA);
   }
 
   // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2.
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     bf16* orow = o + (head0 * Sq + row) * D;
@@ -459,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx * c);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float corr = exp2_hw(m_run - m_use);
@@ -488,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     }
   }
 
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     float* orow = o + (head0 * Sq + row) * D;
