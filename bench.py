@@ -33,6 +33,35 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (dense bf16)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQA"
 
+# Measured HBM bytes per launch of the dominant kernels: two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) on `bench.py --only prefill|decode`,
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (`bench.py --only copy`: FETCH_SIZE reads 0.5x the copied bytes, WRITE_SIZE 1.0x).
+# Each entry holds for the kernel sources whose hash it records; after any change to
+# them the bench reports traffic as null until the counters are taken again.
+# Summary and commands: profiles/gqa70b_hbm_traffic.md.
+FETCH_SCALE = 0.5
+WRITE_SCALE = 1.0
+TRAFFIC = {
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "7cdc64eee1e3970c",
+                "fetch_kib": 162340, "write_kib": 133213},
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "9a4940cc0f905654",
+               "fetch_kib": 262500 + 4155, "write_kib": 8737 + 72},
+}
+
+
+def measured_traffic(name):
+    """HBM bytes per launch (fetch + write, copy-calibrated), or None if stale."""
+    import hashlib
+    t = TRAFFIC[name]
+    m = hashlib.sha256()
+    for f in t["sources"]:
+        with open(os.path.join(ROOT, "streaming_attention_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    if m.hexdigest()[:16] != t["sha256_16"]:
+        return None
+    return int(t["fetch_kib"] * 1024 / FETCH_SCALE + t["write_kib"] * 1024 / WRITE_SCALE)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -40,8 +69,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
-                    help="run only one half of the step (for per-kernel profiling runs)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="run only one half of the step (for per-kernel profiling runs); 'copy' runs a "
+                         "plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -105,6 +135,15 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.warmup + args.steps}))
+        return
     wp = W.GQA70B_PREFILL
     wd = W.GQA70B_DECODE
 
@@ -188,7 +227,10 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill"),
+            "traffic_unit": "HBM bytes per launch (fetch + write)",
+            "algorithmic_min_bytes": 2 * (2 * wp.B * wp.Hq * wp.Sq * wp.d + 2 * wp.B * wp.Hkv * wp.Skv * wp.d)
+                                     + 4 * wp.B * wp.Hq * wp.Sq,
         },
         "roofline_decode": {
             "bound": "hbm",
@@ -197,7 +239,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dc_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode"),
+            "traffic_unit": "HBM bytes per step, split + combine (fetch + write)",
+            "algorithmic_bytes": kv_bytes,
         },
         "device": torch.cuda.get_device_name(dev),
     }
