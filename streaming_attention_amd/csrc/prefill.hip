@@ -43,9 +43,10 @@
 namespace sa {
 namespace {
 
-constexpr int kBM = 128;   // stacked query rows per workgroup
+constexpr int kBM = 128;   // stacked query rows per workgroup (fp32 path)
 constexpr int kBN = 64;    // keys per KV tile (bf16 path)
 constexpr int kThreads = 256;
+constexpr int kNumCUs = 256;          // MI355X compute units
 constexpr float kRescaleLog2 = 8.f;   // lazy-rescale threshold (log2 units)
 constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
 
@@ -62,6 +63,7 @@ struct TileCoord {
 // Workgroup index -> (batch, KV head, M tile).  Heaviest M tiles (latest query
 // positions) are dealt first; with n_groups % 8 == 0 each group is pinned to
 // XCD (group % 8).
+template <int BM>
 __device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int Hkv, int n_mt, int G,
                                               int Sq) {
   int group, rk;
@@ -74,8 +76,8 @@ __device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int Hkv, int
     rk = wg / n_groups;
   }
   int mt;
-  if (Sq % kBM == 0) {
-    const int n_pb = Sq / kBM;         // position blocks per query head
+  if (Sq % BM == 0) {
+    const int n_pb = Sq / BM;          // position blocks per query head
     const int pb = n_pb - 1 - rk / G;  // latest positions first
     const int g = rk % G;
     mt = g * n_pb + pb;
@@ -103,14 +105,22 @@ __device__ __forceinline__ void row_range_positions(int rA, int rB, int Sq, int&
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
+//
+// QB = 32-row query blocks per wave (workgroup = 4 waves = 128 * QB stacked
+// rows).  QB = 2 halves the LDS bytes per MFMA (every K and V fragment read
+// from LDS feeds one MFMA per query block) at the cost of one wave per SIMD
+// (the output accumulators then live in AGPRs); QB = 1 runs two waves per SIMD
+// and suits problems with too few row tiles to fill the chip at QB = 2.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+template <int D, bool CAUSAL, int QB>
+__global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
     float c) {
-  constexpr int KP = D + 8;        // K tile row pitch (elements): 16 B pad
-  constexpr int VP = kBN + 8;      // V^T tile row pitch (elements): 16 B pad
+  constexpr int BM = 128 * QB;           // stacked query rows per workgroup
+  constexpr int RW = 32 * QB;            // rows per wave
+  constexpr int KP = D + 8;              // K tile row pitch (elements): 16 B pad
+  constexpr int VP = kBN + 8;            // V^T tile row pitch (elements): 16 B pad
   constexpr int K_ELEMS = kBN * KP;
   constexpr int V_ELEMS = D * VP;
   constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
@@ -126,16 +136,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   const int G = Hq / Hkv;
   const int rows_total = G * Sq;
-  const int n_mt = (rows_total + kBM - 1) / kBM;
+  const int n_mt = (rows_total + BM - 1) / BM;
   const int n_groups = B * Hkv;
-  const TileCoord tc = map_tile(blockIdx.x, n_groups, Hkv, n_mt, G, Sq);
-  const int r0 = tc.mt * kBM;
+  const TileCoord tc = map_tile<BM>(blockIdx.x, n_groups, Hkv, n_mt, G, Sq);
+  const int r0 = tc.mt * BM;
   const int q_start = Skv - Sq;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
-  const int lr = l & 31;   // query column owned by this lane inside the wave
+  const int lr = l & 31;   // query column owned by this lane inside each row block
   const int hf = l >> 5;   // which half of the key set / d chunk the lane holds
 
   const size_t head0 = (size_t)tc.b * Hq + (size_t)tc.kvh * G;   // first query head of group
@@ -144,19 +154,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const bf16* kg = k + kvoff;
   const bf16* vg = v + kvoff;
 
-  // This lane's query row and its global position.
-  const int row = r0 + 32 * w + lr;
-  const bool row_ok = row < rows_total;
-  const int pos = q_start + (row_ok ? row % Sq : 0);
+  // This lane's query rows (one per row block) and their global positions.
+  int row[QB], pos[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    row[qb] = r0 + RW * w + 32 * qb + lr;
+    pos[qb] = q_start + (row[qb] < rows_total ? row[qb] % Sq : 0);
+  }
 
   // Causal extents: loop bound for the workgroup, mask-free bound per wave.
   int n_tiles = (Skv + kBN - 1) / kBN;
   int wave_tmin = 0x3fffffff;
   if (CAUSAL) {
     int tmin, tmax;
-    row_range_positions(r0, min(r0 + kBM - 1, rows_total - 1), Sq, tmin, tmax);
+    row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, tmin, tmax);
     n_tiles = min(n_tiles, (q_start + tmax) / kBN + 1);
-    const int wA = r0 + 32 * w, wB = min(r0 + 32 * w + 31, rows_total - 1);
+    const int wA = r0 + RW * w, wB = min(r0 + RW * w + RW - 1, rows_total - 1);
     if (wA <= wB) {
       int a, bb;
       row_range_positions(wA, wB, Sq, a, bb);
@@ -164,12 +177,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   }
 
-  // Q^T B operand: lane holds Q[row][16 s + 8 hf .. +7] for s = 0 .. DS-1.
+  // Q^T B operands: lane holds Q[row][16 s + 8 hf .. +7] for s = 0 .. DS-1.
   // Buffer loads: rows past the group's last stacked row read as zero.
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)rows_total * D * 2);
-  bf16x8 qf[DS];
+  bf16x8 qf[QB][DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(buf_ld16(rq, (uint32_t)row * D * 2 + 16 * hf + 32 * s, 0));
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qf[qb][s] = as_bf16x8(buf_ld16(rq, (uint32_t)row[qb] * D * 2 + 16 * hf + 32 * s, 0));
 
   // Staging registers for one K tile and one V tile.
   u32x4 kst[NK];
@@ -231,100 +247,130 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  // S^T = K Q^T for the two 32-key blocks of the tile in K buffer `buf`.
-  auto scores = [&](int buf, f32x16 (&S)[2]) {
+  // S^T = K Q^T for the two 32-key blocks of the tile in K buffer `buf`, for
+  // every row block: each K fragment read from LDS feeds QB MFMAs.
+  auto scores = [&](int buf, f32x16 (&S)[QB][2]) {
     const bf16* Ks = Kring + buf * K_ELEMS;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) S[kb][j] = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) S[qb][kb][j] = 0.f;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + lr) * KP + 16 * s + 8 * hf);
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], S[qb][kb], 0, 0, 0);
       }
     }
   };
 
-  // Running state (per lane = per query row, partial over this lane's keys for l).
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  f32x16 oacc[DB];
+  // Running state per row block (per lane = per query row; l is this lane's
+  // partial over its half of the keys).
+  float m_run[QB], l_run[QB];
+  f32x16 oacc[QB][DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[qb][i][j] = 0.f;
+  }
 
-  // One pipelined step: mask and softmax of tile kt (scores in S), the score
-  // MFMAs of tile kt + 1 (into Snext, from K buffer kbuf_next; after the last
-  // tile they run on an idle buffer and are discarded, which keeps them in the
-  // same basic block as the softmax they interleave with), then
-  // O^T += V^T P^T for tile kt (V^T buffer vbuf).
-  auto step = [&](int kt, f32x16 (&S)[2], f32x16 (&Snext)[2], int kbuf_next, int vbuf) {
-    // P1: boundary mask (tail of the key range, causal diagonal) as a select
-    // to -inf, then the row max and the lazy-rescale decision.
+  // Row max of a score tile, scaled to log2 units (c > 0), combined with the
+  // partner lane that holds the other half of the tile's keys.
+  auto tile_max = [&](const f32x16 (&S)[2]) { return max_xor32(max_of32(S[0], S[1])) * c; };
+
+  // One pipelined step for tile kt, whose scores S and unmasked scaled row max
+  // mx were produced by the previous step:
+  //   P1  mask (straddling / tail tiles only, then the max is recomputed) and
+  //       the lazy-rescale decision;
+  //   P2  score MFMAs of tile kt + 1 (into Snext, from K buffer kbuf_next)
+  //       interleaved with this tile's exponentials and half of its bf16
+  //       packing;
+  //   P3  O^T += V^T P^T (V^T buffer vbuf) interleaved with the other half of
+  //       the packing, the row sums and the row max of tile kt + 1.
+  // After the last tile the score MFMAs run on an idle buffer and are
+  // discarded, which keeps them in the same basic block as the work they
+  // interleave with.
+  auto step = [&](int kt, f32x16 (&S)[QB][2], f32x16 (&Snext)[QB][2], float (&mx)[QB], int kbuf_next,
+                  int vbuf) {
     const int key_end = kt * kBN + kBN - 1;
     const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = (key < Skv) && (!CAUSAL || key <= pos);
-          S[kb][r] = vis ? S[kb][r] : kNegInf;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool vis = (key < Skv) && (!CAUSAL || key <= pos[qb]);
+            S[qb][kb][r] = vis ? S[qb][kb][r] : kNegInf;
+          }
+        mx[qb] = tile_max(S[qb]);
+      }
     }
-    // Online softmax in base 2 (c = scale * log2 e > 0).  The running max used
-    // as the exponent base is only raised when a row's tile max exceeds it by
-    // more than kRescaleLog2 (then O and l are rescaled); otherwise P may reach
-    // 2^kRescaleLog2, which fp32 and bf16 hold exactly enough.  O and l always
-    // share the same base, so O / l is unchanged (the rescale is skipped, not
-    // approximated).
-    const float mloc = max_of32(S[0], S[1]);
-    const float mx = max_xor32(mloc) * c;
-    const bool grow = mx > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float corr = exp2_hw(m_run - m_new);   // 0 when m_run = -inf, 1 when unchanged
-      l_run *= corr;
+    // Online softmax in base 2.  The running max used as the exponent base is
+    // only raised when a row's tile max exceeds it by more than kRescaleLog2
+    // (then O and l are rescaled); otherwise P may reach 2^kRescaleLog2, which
+    // fp32 and bf16 hold exactly enough.  O and l always share the same base,
+    // so O / l is unchanged (the rescale is skipped, not approximated).
+    float m_use[QB];
 #pragma unroll
-      for (int i = 0; i < DB; ++i)
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool grow = mx[qb] > m_run[qb] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx[qb] : m_run[qb];
+        const float corr = exp2_hw(m_run[qb] - m_new);   // 0 when m_run = -inf, 1 when unchanged
+        l_run[qb] *= corr;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[i][j] *= corr;
-      m_run = m_new;
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[qb][i][j] *= corr;
+        m_run[qb] = m_new;
+      }
+      m_use[qb] = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
     }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 
-    // P2: next tile's score MFMAs interleaved with this tile's exponentials
-    // and bf16 packing (independent work: the VALU runs while the MFMAs do).
+    // P2.
     scores(kbuf_next, Snext);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[kb][r] = exp2_hw(__builtin_fmaf(S[kb][r], c, -m_use));
-    bf16x8 pf[2][2];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) S[qb][kb][r] = exp2_hw(__builtin_fmaf(S[qb][kb][r], c, -m_use[qb]));
+    bf16x8 pf[QB][2][2];
+    auto pack = [&](int kb) {
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int r8 = 8 * cc;
-        pf[kb][cc] = to_bf16x8(S[kb][r8 + 0], S[kb][r8 + 1], S[kb][r8 + 2], S[kb][r8 + 3],
-                               S[kb][r8 + 4], S[kb][r8 + 5], S[kb][r8 + 6], S[kb][r8 + 7]);
-      }
-    // Schedule: LDS reads run kLdsAhead fragments ahead of their MFMA.
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int r8 = 8 * cc;
+          pf[qb][kb][cc] = to_bf16x8(S[qb][kb][r8 + 0], S[qb][kb][r8 + 1], S[qb][kb][r8 + 2], S[qb][kb][r8 + 3],
+                                     S[qb][kb][r8 + 4], S[qb][kb][r8 + 5], S[qb][kb][r8 + 6], S[qb][kb][r8 + 7]);
+        }
+    };
+    pack(0);
+    // Schedule: LDS reads run kLdsAhead fragments ahead of their MFMAs.
     __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
 #pragma unroll
     for (int i = 0; i < 2 * DS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);                  // QB MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x002, 5 * QB, 0);   // 5 VALU each
       if (i + kLdsAhead < 2 * DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
     }
 
-    // P3: O^T += V^T P^T, interleaved with the row-sum tree.
+    // P3.
     const bf16* Vs = Vring + vbuf * V_ELEMS;
+    pack(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -332,28 +378,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + (32 * db + lr) * VP + 32 * kb + 16 * cc + 8 * hf);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][cc], oacc[db], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][cc], oacc[qb][db], 0, 0, 0);
         }
-    l_run += sum_tree32(S[0], S[1]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      l_run[qb] += sum_tree32(S[qb][0], S[qb][1]);
+      mx[qb] = tile_max(Snext[qb]);
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // QB MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * QB, 0);   // 4 VALU each
       if (i + kLdsAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
     }
   };
 
   // Software pipeline (the pages' "issue the next Q K^T before this tile's
-  // softmax"): K runs one tile ahead of V.  In iteration kt a wave issues the
-  // score MFMAs of tile kt + 1, then the softmax of tile kt (independent VALU
-  // work that executes while those MFMAs run), then the P V MFMAs of tile kt.
-  // K tile kt + 2 and V tile kt + 1 are loaded during the iteration and stored
-  // into the buffers that iteration kt - 1 finished reading; one barrier per
-  // tile orders the rings.
+  // softmax"): K runs one tile ahead of V.  K tile kt + 2 and V tile kt + 1 are
+  // loaded during iteration kt and stored into the buffers that iteration
+  // kt - 1 finished reading; one barrier per tile orders the rings.
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
   wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
-  f32x16 sA[2], sB[2];
+  f32x16 sA[QB][2], sB[QB][2];
+  float mx[QB];
   if (n_tiles > 0) {
     load_k(0);
     load_v(0);
@@ -363,12 +413,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     store_k(1);
     __syncthreads();
     scores(0, sA);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = tile_max(sA[qb]);
     __syncthreads();   // K buffer 0 is rewritten in iteration 0
   }
-  auto iteration = [&](int kt, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+  auto iteration = [&](int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
     load_k(kt + 2);    // past the last tile these read zeros, stored into idle buffers
     load_v(kt + 1);
-    step(kt, Scur, Snext, (kt + 1) & 1, kt & 1);
+    step(kt, Scur, Snext, mx, (kt + 1) & 1, kt & 1);
     store_k(kt & 1);
     store_v((kt + 1) & 1);
     __syncthreads();
@@ -379,24 +431,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   }
 
   // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2.
-  const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_ok) {
-    bf16* orow = o + (head0 * Sq + row) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = sum_xor32(l_run[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row[qb] < rows_total) {
+      bf16* orow = o + (head0 * Sq + row[qb]) * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hf;
-        const uint32_t lo = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 0] * inv)),
-                                    __builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 1] * inv)));
-        const uint32_t hi = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 2] * inv)),
-                                    __builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 3] * inv)));
-        u32x2 pr = {lo, hi};
-        *reinterpret_cast<u32x2*>(orow + d0) = pr;
-      }
-    if (lse != nullptr && hf == 0)
-      lse[head0 * Sq + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hf;
+          const uint32_t lo = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 0] * inv)),
+                                      __builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 1] * inv)));
+          const uint32_t hi = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 2] * inv)),
+                                      __builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 3] * inv)));
+          u32x2 pr = {lo, hi};
+          *reinterpret_cast<u32x2*>(orow + d0) = pr;
+        }
+      if (lse != nullptr && hf == 0)
+        lse[head0 * Sq + row[qb]] = l_tot > 0.f ? (m_run[qb] + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -424,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
   const int G = Hq / Hkv;
   const int rows_total = G * Sq;
   const int n_mt = (rows_total + kBM - 1) / kBM;
-  const TileCoord tc = map_tile(blockIdx.x, B * Hkv, Hkv, n_mt, G, Sq);
+  const TileCoord tc = map_tile<kBM>(blockIdx.x, B * Hkv, Hkv, n_mt, G, Sq);
   const int r0 = tc.mt * kBM;
   const int q_start = Skv - Sq;
 
@@ -564,34 +619,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const int G = a.Hq / a.Hkv;
-  const long long n_mt = ((long long)G * a.Sq + kBM - 1) / kBM;
-  const long long grid = n_mt * (long long)a.B * a.Hkv;
+  const long long rows = (long long)(a.Hq / a.Hkv) * a.Sq;   // stacked rows per (batch, KV head)
+  const long long groups = (long long)a.B * a.Hkv;
   const float c = a.scale * kLog2e;
-  const dim3 g((unsigned)grid), blk(kThreads);
-#define SA_LAUNCH_BF16(DD, CC)                                                                      \
-  hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC>), g, blk, 0, stream, (const bf16*)a.q,          \
-                     (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, \
+  const dim3 blk(kThreads);
+  if (a.bf16) {
+    // One 32-row block per wave.  (Two blocks per wave halve the LDS bytes per
+    // MFMA but, at one wave per SIMD, measured slower on the 70B-shape prefill:
+    // 756 vs 941 TFLOP/s, the compiler shuttling accumulators between AGPRs
+    // and VGPRs.)
+    const dim3 g((unsigned)((rows + 127) / 128 * groups));
+#define SA_LAUNCH_BF16(DD, CC, QQ)                                                                      \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, QQ>), g, blk, 0, stream, (const bf16*)a.q,          \
+                     (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,     \
                      a.Skv, c)
+    if (a.d == 128) {
+      if (a.causal) {
+        SA_LAUNCH_BF16(128, true, 1);
+      } else {
+        SA_LAUNCH_BF16(128, false, 1);
+      }
+    } else {
+      if (a.causal) {
+        SA_LAUNCH_BF16(64, true, 1);
+      } else {
+        SA_LAUNCH_BF16(64, false, 1);
+      }
+    }
+#undef SA_LAUNCH_BF16
+  } else {
+    const dim3 g((unsigned)((rows + kBM - 1) / kBM * groups));
 #define SA_LAUNCH_F32(DD, CC)                                                                         \
   hipLaunchKernelGGL((prefill_f32_kernel<DD, CC>), g, blk, 0, stream, (const float*)a.q,            \
                      (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, \
                      a.Skv, c)
-  if (a.bf16) {
-    if (a.d == 128) {
-      if (a.causal) SA_LAUNCH_BF16(128, true); else SA_LAUNCH_BF16(128, false);
-    } else {
-      if (a.causal) SA_LAUNCH_BF16(64, true); else SA_LAUNCH_BF16(64, false);
-    }
-  } else {
     if (a.d == 128) {
       if (a.causal) SA_LAUNCH_F32(128, true); else SA_LAUNCH_F32(128, false);
     } else {
       if (a.causal) SA_LAUNCH_F32(64, true); else SA_LAUNCH_F32(64, false);
     }
-  }
-#undef SA_LAUNCH_BF16
 #undef SA_LAUNCH_F32
+  }
   return hipGetLastError();
 }
 
