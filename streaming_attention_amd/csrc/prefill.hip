@@ -339,7 +339,9 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
       m_use[qb] = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
     }
 
-    // P2.
+    // P2.  The wave raises its issue priority while it feeds the matrix core
+    // (P2 + P3), so the arbiter prefers its MFMAs over the other wave's VALU.
+    __builtin_amdgcn_s_setprio(1);
     scores(kbuf_next, Snext);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -394,6 +396,7 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
       __builtin_amdgcn_sched_group_barrier(0x002, 4 * QB, 0);   // 4 VALU each
       if (i + kLdsAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Software pipeline (the pages' "issue the next Q K^T before this tile's
