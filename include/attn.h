@@ -1,7 +1,7 @@
 /*
  * Streaming attention forward for AMD Instinct MI355X (gfx950): C ABI.
  *
- * Three entry points compute softmax(scale * Q K^T + causal mask) V tile by
+ * The entry points compute softmax(scale * Q K^T + causal mask) V tile by
  * tile with an online softmax (running max m, running sum l, rescaled output
  * O), so the score and probability matrices never reach memory:
  *
@@ -9,6 +9,7 @@
  *   attn_decode_splitkv  one query token per sequence, the KV range cut into
  *                        splits that each yield a partial result
  *   attn_combine_lse     merge of the split partials by log-sum-exp
+ *   attn_decode          the split-KV decode and the merge in one launch
  *
  * The method is the one of "ADR-0060: AHBM GQA Fused Attention kernel
  * (Llama3-70B)": per-tile online softmax (its section 3), log-sum-exp merge of
@@ -140,6 +141,35 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
                         int32_t max_splits, int32_t dtype, float scale,
                         float* part_o, float* part_lse, void* stream);
+
+/*
+ * attn_decode -- split-KV decode and the log-sum-exp merge in one launch.
+ *
+ * Same computation, arguments and split plan as attn_decode_splitkv followed
+ * by attn_combine_lse, fused: every split workgroup of a (sequence, KV head)
+ * writes its partial and counts itself in; the last one to arrive merges that
+ * group's partials and writes the final output.  Nothing waits on anything
+ * (ADR-0060 section 4.3: a node merges as its children arrive, and the root
+ * normalises once).  This saves the second launch and its ramp.
+ *
+ *   (q ... part_lse)  exactly as for attn_decode_splitkv; part_o / part_lse
+ *                     are the workspace the splits publish into (and hold the
+ *                     partials afterwards)
+ *   counters   [B * Hkv] int32 device workspace.  Must be all zero on entry;
+ *              every entry is zero again when the launch has completed.
+ *              Launches that share a counters buffer must not overlap.
+ *   o          [B, Hq, 1, d] bf16 (written)
+ *   lse        [B, Hq] float32 (written); may be NULL
+ *
+ * A sequence with kv_len = 0 gets O = 0 and LSE = -inf.
+ * Errors: as attn_decode_splitkv, plus ATTN_ERR_NULL for counters or o.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* kv_len, const int32_t* num_splits,
+                int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
+                int32_t max_splits, int32_t dtype, float scale,
+                float* part_o, float* part_lse, int32_t* counters,
+                void* o, float* lse, void* stream);
 
 /*
  * attn_combine_lse -- merge split partials into the final decode output.

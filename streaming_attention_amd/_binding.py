@@ -33,6 +33,7 @@ SIGNATURES = {
     "attn_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P], ctypes.c_int),
     "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], ctypes.c_int),
     "attn_combine_lse": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], ctypes.c_int),
+    "attn_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -197,11 +198,76 @@ def combine_lse(part_o, part_lse, num_splits=None, out_dtype=torch.bfloat16, out
     return out, lse
 
 
+_COUNTERS = {}
+
+
+def _counters_for(device, n):
+    """A zeroed int32 counter workspace of at least n entries, cached per device.
+
+    attn_decode leaves it zero again after every launch, so it can be reused by
+    launches that are ordered on one stream.  Callers that launch concurrently
+    on several streams pass their own buffers.
+    """
+    t = _COUNTERS.get(device)
+    if t is None or t.numel() < n:
+        t = torch.zeros(max(n, 256), dtype=torch.int32, device=device)
+        _COUNTERS[device] = t
+    return t
+
+
 def decode(q, k_cache, v_cache, kv_len=None, num_splits=None, max_splits: int = 64,
-           scale: float | None = None, part_o=None, part_lse=None, out=None, lse=None):
-    """Split-KV decode followed by the log-sum-exp combine: ``(o, lse)``."""
-    po, pl = decode_splitkv(q, k_cache, v_cache, kv_len, num_splits, max_splits, scale, part_o, part_lse)
-    return combine_lse(po, pl, num_splits, q.dtype, out, lse)
+           scale: float | None = None, part_o=None, part_lse=None, out=None, lse=None,
+           counters=None, fused: bool = False):
+    """Split-KV decode followed by the log-sum-exp merge: ``(o, lse)``.
+
+    ``fused=False`` (default) runs ``attn_decode_splitkv`` then
+    ``attn_combine_lse`` -- the faster path for large decodes.  ``fused=True``
+    runs both in one launch (``attn_decode``; ``counters`` is an int32
+    workspace of ``B * Hkv`` zeros, a cached one when None).
+    """
+    if not fused:
+        po, pl = decode_splitkv(q, k_cache, v_cache, kv_len, num_splits, max_splits, scale, part_o, part_lse)
+        return combine_lse(po, pl, num_splits, q.dtype, out, lse)
+    _need(q, "q", 4, torch.bfloat16)
+    _need(k_cache, "k_cache", 4, torch.bfloat16, q.device)
+    _need(v_cache, "v_cache", 4, torch.bfloat16, q.device)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per sequence: q must be [B,Hq,1,d]")
+    Hkv, S_cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, S_cap, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    for name, t in (("kv_len", kv_len), ("num_splits", num_splits)):
+        if t is not None:
+            _need(t, name, 1, torch.int32, q.device)
+            if t.shape[0] != B:
+                raise ValueError(f"{name} must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if part_o is None:
+        part_o = torch.empty((B, Hq, max_splits, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, max_splits), dtype=torch.float32, device=q.device)
+    _need(part_o, "part_o", 4, torch.float32, q.device)
+    _need(part_lse, "part_lse", 3, torch.float32, q.device)
+    if tuple(part_o.shape) != (B, Hq, max_splits, d) or tuple(part_lse.shape) != (B, Hq, max_splits):
+        raise ValueError("partial buffers must be [B,Hq,max_splits,d] and [B,Hq,max_splits]")
+    if counters is None:
+        counters = _counters_for(q.device, B * Hkv)
+    _need(counters, "counters", 1, torch.int32, q.device)
+    if counters.numel() < B * Hkv:
+        raise ValueError("counters must hold B * Hkv entries")
+    if out is None:
+        out = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", 4, torch.bfloat16, q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", 2, torch.float32, q.device)
+    st = lib().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(num_splits),
+                           B, Hq, Hkv, S_cap, d, int(max_splits), ATTN_DTYPE_BF16, float(scale),
+                           _ptr(part_o), _ptr(part_lse), _ptr(counters), _ptr(out), _ptr(lse), _stream(q))
+    _check(st, "attn_decode")
+    return out, lse
 
 
 def splits_for_lengths(lens, keys_per_split: int = 2048, max_splits: int = 64):

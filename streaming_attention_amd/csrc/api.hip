@@ -79,6 +79,35 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   a.q = q; a.k = k_cache; a.v = v_cache; a.kv_len = kv_len; a.num_splits = num_splits;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_cap = S_cap; a.d = d; a.max_splits = max_splits;
   a.scale = scale; a.part_o = part_o; a.part_lse = part_lse;
+  a.counters = nullptr; a.o = nullptr; a.lse = nullptr;
+  return sa::launch_decode_splitkv(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+                                                                                            : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                const int32_t* num_splits, int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
+                int32_t max_splits, int32_t dtype, float scale, float* part_o, float* part_lse, int32_t* counters,
+                void* o, float* lse, void* stream) {
+  if (B < 0 || S_cap < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
+  if (!good_scale(scale)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv * max_splits > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (B == 0) return ATTN_OK;
+  if (q == nullptr || part_o == nullptr || part_lse == nullptr || counters == nullptr || o == nullptr)
+    return ATTN_ERR_NULL;
+  if (S_cap > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(part_o) || !aligned16(part_lse) || !aligned16(counters) || !aligned16(o) ||
+      !aligned16(lse) || (S_cap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return ATTN_ERR_ALIGN;
+
+  sa::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_len = kv_len; a.num_splits = num_splits;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_cap = S_cap; a.d = d; a.max_splits = max_splits;
+  a.scale = scale; a.part_o = part_o; a.part_lse = part_lse;
+  a.counters = counters; a.o = o; a.lse = lse;
   return sa::launch_decode_splitkv(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
                                                                                             : ATTN_ERR_LAUNCH;
 }

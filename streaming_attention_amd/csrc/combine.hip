@@ -9,12 +9,10 @@
 // valid merge order.
 //
 // MI355X mapping: one workgroup (4 waves) per (sequence, query head) row.  The
-// row's split maximum M is a workgroup reduction over part_lse.  Wave w then
-// accumulates splits w, w + 4, ... with all its partial-row loads issued before
-// they are consumed (the loop is unrolled), each lane owning D / 64 output
-// elements, and the four wave sums are added through LDS.  The kernel is
-// latency-bound (a few MB in total), so the point is to keep many independent
-// loads in flight, not to stream.
+// kernel is latency-bound (a few MB in total), so every load of a row is issued
+// in one round: the split lse values (one per thread, for the workgroup max M)
+// and, per wave, up to 16 partial rows (splits w, w + 4, ...; each lane owns
+// D / 64 output elements).  The four wave sums are added through LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -22,7 +20,7 @@ namespace sa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restrict__ part_o,
@@ -40,10 +38,22 @@ __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restric
   const int b = row / Hq;
   int n = num_splits ? num_splits[b] : max_splits;
   n = n < 1 ? 1 : (n > max_splits ? max_splits : n);
-
-  // M = max over the row's split lse values (n <= 256 = one value per thread).
   const float* L = part_lse + (size_t)row * max_splits;
+  const float* Op = part_o + (size_t)row * max_splits * D + PER * l;
+
+  // Every load of the row is issued up front, in one memory round: the split
+  // lse values for the maximum (n <= 256, one per thread) and this wave's
+  // first kUnroll partial rows.
   float M = tid < n ? L[tid] : kNegInf;
+  float lv[kUnroll];
+  float ov[kUnroll][PER];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int s = w + kWaves * u;
+    lv[u] = s < n ? L[s] : kNegInf;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ov[u][i] = s < n ? Op[(size_t)s * D + i] : 0.f;
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   if (l == 0) red[w] = M;
@@ -54,25 +64,22 @@ __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restric
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float wsum = 0.f;
-  if (M != kNegInf) {
-    const float* Op = part_o + (size_t)row * max_splits * D + PER * l;
-    for (int s0 = w; s0 < n; s0 += kWaves * kUnroll) {
-      float lv[kUnroll];
-      float ov[kUnroll][PER];
+  const float Mb = (M == kNegInf) ? 0.f : M;   // all splits empty: every weight is exp2(-inf) = 0
+  for (int s0 = w;; s0 += kWaves * kUnroll) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int s = s0 + kWaves * u;
-        lv[u] = s < n ? L[s] : kNegInf;
+    for (int u = 0; u < kUnroll; ++u) {
+      const float wgt = exp2_hw((lv[u] - Mb) * kLog2e);
+      wsum += wgt;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) ov[u][i] = s < n ? Op[(size_t)s * D + i] : 0.f;
-      }
+      for (int i = 0; i < PER; ++i) acc[i] += wgt * ov[u][i];
+    }
+    if (s0 + kWaves * kUnroll >= n) break;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float wgt = exp2_hw((lv[u] - M) * kLog2e);   // exp2(-inf) = 0 for empty splits
-        wsum += wgt;
+    for (int u = 0; u < kUnroll; ++u) {   // next batch of splits (rarely needed: n > 32)
+      const int s = s0 + kWaves * kUnroll + kWaves * u;
+      lv[u] = s < n ? L[s] : kNegInf;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += wgt * ov[u][i];
-      }
+      for (int i = 0; i < PER; ++i) ov[u][i] = s < n ? Op[(size_t)s * D + i] : 0.f;
     }
   }
 #pragma unroll

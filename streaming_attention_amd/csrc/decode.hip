@@ -29,7 +29,8 @@
 namespace sa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;           // waves per workgroup
+constexpr bool kKViaLds = true;     // K loaded row-coalesced and staged through LDS
 constexpr int kChunk = 32;          // keys per wave iteration
 constexpr int kSplitGranule = 64;   // split boundaries are multiples of this
 
@@ -42,17 +43,115 @@ struct DecodeCfg {
   static constexpr int NGRP = 8 / LQ;        // 4-key groups per lane (2 or 1)
   static constexpr int VTP = kChunk + 8;     // V^T row pitch (elements), 80 B
   static constexpr int VT_ELEMS = D * VTP;   // per wave
+  static constexpr int KP = D + 8;           // K row pitch in LDS (elements), 16 B pad
+  static constexpr int K_ELEMS = kKViaLds ? kChunk * KP : 0;   // per wave
+  static constexpr int K_RPI = 64 / CPR;     // K rows per coalesced load instruction
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
+// A split's partial is written with a plain store, or with a device-scope store
+// when the same launch merges it (see arrive_and_merge).
+template <bool DEVICE_SCOPE>
+__device__ __forceinline__ void publish(float* p, float v) {
+  if constexpr (DEVICE_SCOPE) st_dev(p, v); else *p = v;
+}
+
+// Fused merge (attn_decode).  Every split workgroup of a (sequence, KV head)
+// publishes its partials and counts itself in; the one that arrives last merges
+// the group's n partials with the log-sum-exp rule (M = max lse_s,
+// w_s = e^{lse_s - M}, O = sum w_s O_s / sum w_s, LSE = M + ln sum w_s) and
+// resets the counter for the next call.  Nothing waits: a workgroup that is not
+// last simply exits ("ADR-0060: AHBM GQA Fused Attention kernel", section 4.3:
+// nodes merge as their children arrive and the root normalises once).
+//
+// Publication without a device-wide fence (which on this multi-XCD part writes
+// back and invalidates the whole L2 of the workgroup's XCD): the partials are
+// written with device-scope (sc1) stores, every thread waits until its stores
+// have completed, the workgroup synchronises, and one relaxed device-scope
+// atomic counts it in.  The last arriver reads the partials with device-scope
+// loads, so no stale L2 copy from an earlier call can be returned.
+template <int D, int NT>
+__device__ void arrive_and_merge(unsigned char* smem, int32_t* counters, const float* part_o,
+                                 const float* part_lse, bf16* o, float* lse, int b, int kvh, int Hkv, int G,
+                                 size_t head0, int n, int max_splits) {
+  constexpr int DQ = D / 4;          // 16-byte column groups of a partial row
+  constexpr int kBatch = 32;         // partial rows in flight per thread
+  const int tid = threadIdx.x;
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's device-scope partial stores have completed
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(&counters[b * Hkv + kvh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              n - 1;
+  __syncthreads();
+  if (!is_last) return;
+
+  // Split weights of each head into LDS: w[j][s] = e^{lse_js - M_j}.
+  float* wts = reinterpret_cast<float*>(smem);            // [G][n]
+  float* Mh = wts + G * n;                                 // [G]
+  float* Wsum = Mh + G;                                    // [G]
+  for (int i = tid; i < G * n; i += NT)
+    wts[i] = ld_dev(part_lse + (head0 + i / n) * max_splits + i % n);
+  __syncthreads();
+  if (tid < G) {
+    float M = kNegInf;
+    for (int s2 = 0; s2 < n; ++s2) M = fmaxf(M, wts[tid * n + s2]);
+    Mh[tid] = M;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * n; i += NT) {
+    const float M = Mh[i / n];
+    wts[i] = M == kNegInf ? 0.f : exp2_hw((wts[i] - M) * kLog2e);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float ws = 0.f;
+    for (int s2 = 0; s2 < n; ++s2) ws += wts[tid * n + s2];
+    Wsum[tid] = ws;
+    if (lse != nullptr) lse[head0 + tid] = ws > 0.f ? Mh[tid] + __logf(ws) : kNegInf;
+  }
+  __syncthreads();
+
+  // O[j][4 dq .. 4 dq + 3] = sum_s w[j][s] O_s[j][...] / sum_s w[j][s].
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(part_o + head0 * max_splits * D, (uint32_t)(G * max_splits * D * 4));
+  for (int item = tid; item < G * DQ; item += NT) {
+    const int j = item / DQ, dq = item % DQ;
+    const uint32_t voff = (uint32_t)((j * max_splits * D + 4 * dq) * 4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n; s0 += kBatch) {
+      f32x4 x[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        x[u] = (s0 + u < n) ? buf_ld16_dev(rp, voff, (uint32_t)((s0 + u) * D * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float wgt = (s0 + u < n) ? wts[j * n + s0 + u] : 0.f;
+        acc += wgt * x[u];
+      }
+    }
+    const float ws = Wsum[j];
+    const float inv = ws > 0.f ? 1.f / ws : 0.f;
+    const uint32_t lo2 = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(acc[0] * inv)),
+                                 __builtin_bit_cast(uint16_t, (bf16)(acc[1] * inv)));
+    const uint32_t hi2 = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(acc[2] * inv)),
+                                 __builtin_bit_cast(uint16_t, (bf16)(acc[3] * inv)));
+    u32x2 pr = {lo2, hi2};
+    *reinterpret_cast<u32x2*>(o + (head0 + j) * D + 4 * dq) = pr;
+  }
+  if (tid == 0)   // ready for the next call
+    __hip_atomic_store(&counters[b * Hkv + kvh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, bool FUSED, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void decode_splitkv_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ num_splits, int B, int Hq,
     int Hkv, int S_cap, int max_splits, float c, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    float* __restrict__ part_lse, int32_t* __restrict__ counters, bf16* __restrict__ o,
+    float* __restrict__ lse) {
   using C = DecodeCfg<D>;
-  constexpr int MERGE_FLOATS = 4 * 16 * D + 2 * 4 * 16;
-  constexpr int SMEM_BYTES_VT = 4 * C::VT_ELEMS * 2;
+  constexpr int kThreads = 64 * NW;
+  constexpr int MERGE_FLOATS = NW * 16 * D + 2 * NW * 16;
+  constexpr int SMEM_BYTES_VT = NW * (C::VT_ELEMS + C::K_ELEMS) * 2;
   constexpr int SMEM_BYTES = SMEM_BYTES_VT > MERGE_FLOATS * 4 ? SMEM_BYTES_VT : MERGE_FLOATS * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
 
@@ -79,9 +178,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
     // Empty split: (lse, O) = (-inf, 0).
     for (int i = tid; i < G * D; i += kThreads) {
       const int j = i / D, d = i % D;
-      part_o[((head0 + j) * max_splits + s) * D + d] = 0.f;
-      if (d == 0) part_lse[(head0 + j) * max_splits + s] = kNegInf;
+      publish<FUSED>(part_o + ((head0 + j) * max_splits + s) * D + d, 0.f);
+      if (d == 0) publish<FUSED>(part_lse + (head0 + j) * max_splits + s, kNegInf);
     }
+    if constexpr (FUSED) arrive_and_merge<D, kThreads>(smem, counters, part_o, part_lse, o, lse, b, kvh, Hkv, G, head0, n,
+                                              max_splits);
     return;
   }
 
@@ -113,13 +214,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
   // Keys past the split end are read clamped to its last key (finite data,
   // masked to -inf in the scores, so P = 0 for them); cache slots at or past
   // kv_len are never touched.  Unconditional loads let the next chunk's loads
-  // stay in flight while the current one is processed.
+  // stay in flight while the current one is processed.  K/V are streamed once,
+  // so the loads are non-temporal.
   auto load_chunk = [&](Regs& R, int key0) {
+    if constexpr (kKViaLds) {
+      // Whole 16-byte columns of full rows per instruction: K_RPI rows each.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(key0 + 16 * kb + j16, hi - 1);
+      for (int i = 0; i < 2 * C::DS; ++i) {
+        const int key = min(key0 + l / C::CPR + C::K_RPI * i, hi - 1);
+        R.k[i / C::DS][i % C::DS] = ld16_nt(kg + (size_t)key * D + 8 * (l % C::CPR));
+      }
+    } else {
 #pragma unroll
-      for (int st = 0; st < C::DS; ++st) R.k[kb][st] = ld16(kg + (size_t)key * D + 32 * st + 8 * qq);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = min(key0 + 16 * kb + j16, hi - 1);
+#pragma unroll
+        for (int st = 0; st < C::DS; ++st) R.k[kb][st] = ld16_nt(kg + (size_t)key * D + 32 * st + 8 * qq);
+      }
     }
 #pragma unroll
     for (int g = 0; g < C::NGRP; ++g) {
@@ -127,12 +238,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = min(key0 + 4 * kgid + r, hi - 1);
-        R.v[g][r] = ld16(vg + (size_t)key * D + 8 * vcol);
+        R.v[g][r] = ld16_nt(vg + (size_t)key * D + 8 * vcol);
       }
     }
   };
 
-  bf16* VT = reinterpret_cast<bf16*>(smem) + w * C::VT_ELEMS;
+  bf16* VT = reinterpret_cast<bf16*>(smem) + w * (C::VT_ELEMS + C::K_ELEMS);
+  bf16* KL = VT + C::VT_ELEMS;   // per-wave K rows (only with kKViaLds)
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4 oacc[C::DB];
@@ -146,12 +258,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
 
     // S^T for keys key0 + 16 kb + (0..15).
     f32x4 sacc[2];
+    if constexpr (kKViaLds) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 2 * C::DS; ++i)
+        st16(KL + (l / C::CPR + C::K_RPI * i) * C::KP + 8 * (l % C::CPR), R.k[i / C::DS][i % C::DS]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < C::DS; ++st)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[kb][st]), qf[st], sacc[kb], 0, 0, 0);
+      for (int st = 0; st < C::DS; ++st) {
+        bf16x8 a;
+        if constexpr (kKViaLds)
+          a = *reinterpret_cast<const bf16x8*>(KL + (16 * kb + j16) * C::KP + 32 * st + 8 * qq);
+        else
+          a = as_bf16x8(R.k[kb][st]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], sacc[kb], 0, 0, 0);
+      }
     }
     if (key0 + kChunk > hi) {
 #pragma unroll
@@ -227,15 +354,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
   Regs ra, rb;
   int ci = w;
   if (ci < nch) load_chunk(ra, lo + ci * kChunk);
-  if (ci + 4 < nch) load_chunk(rb, lo + (ci + 4) * kChunk);
+  if (ci + NW < nch) load_chunk(rb, lo + (ci + NW) * kChunk);
   while (ci < nch) {
     process(ra, ci);
-    if (ci + 8 < nch) load_chunk(ra, lo + (ci + 8) * kChunk);
-    ci += 4;
+    if (ci + 2 * NW < nch) load_chunk(ra, lo + (ci + 2 * NW) * kChunk);
+    ci += NW;
     if (ci >= nch) break;
     process(rb, ci);
-    if (ci + 8 < nch) load_chunk(rb, lo + (ci + 8) * kChunk);
-    ci += 4;
+    if (ci + 2 * NW < nch) load_chunk(rb, lo + (ci + 2 * NW) * kChunk);
+    ci += NW;
   }
 
   // Row sum over the 4 lanes of the query column.
@@ -244,9 +371,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
 
   // Merge the 4 wave states through LDS.
   __syncthreads();
-  float* Ow = reinterpret_cast<float*>(smem);       // [4][16][D] unnormalised O
-  float* mw = Ow + 4 * 16 * D;                        // [4][16]
-  float* lw = mw + 4 * 16;                            // [4][16]
+  float* Ow = reinterpret_cast<float*>(smem);       // [NW][16][D] unnormalised O
+  float* mw = Ow + NW * 16 * D;                       // [NW][16]
+  float* lw = mw + NW * 16;                           // [NW][16]
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -260,19 +387,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
     const int j = i / D, d = i % D;
     float M = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mw[ww * 16 + j]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mw[ww * 16 + j]);
     float osum = 0.f, wsum = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const float f = exp2_hw(mw[ww * 16 + j] - M);
         wsum += f * lw[ww * 16 + j];
         osum += f * Ow[(ww * 16 + j) * D + d];
       }
     }
     const bool has = wsum > 0.f;
-    part_o[((head0 + j) * max_splits + s) * D + d] = has ? osum / wsum : 0.f;
-    if (d == 0) part_lse[(head0 + j) * max_splits + s] = has ? (M + __log2f(wsum)) * kLn2 : kNegInf;
+    publish<FUSED>(part_o + ((head0 + j) * max_splits + s) * D + d, has ? osum / wsum : 0.f);
+    if (d == 0) publish<FUSED>(part_lse + (head0 + j) * max_splits + s, has ? (M + __log2f(wsum)) * kLn2 : kNegInf);
+  }
+  if constexpr (FUSED) {
+    __syncthreads();   // the merge below reuses the LDS staging area
+    arrive_and_merge<D, kThreads>(smem, counters, part_o, part_lse, o, lse, b, kvh, Hkv, G, head0, n, max_splits);
   }
 }
 
@@ -281,15 +412,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_splitkv_bf16_kernel(
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.B * a.Hkv * a.max_splits;
   const float c = a.scale * kLog2e;
-  const dim3 g((unsigned)grid), blk(kThreads);
-  if (a.d == 128)
-    hipLaunchKernelGGL((decode_splitkv_bf16_kernel<128>), g, blk, 0, stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, a.kv_len, a.num_splits, a.B, a.Hq, a.Hkv, a.S_cap, a.max_splits, c,
-                       a.part_o, a.part_lse);
-  else
-    hipLaunchKernelGGL((decode_splitkv_bf16_kernel<64>), g, blk, 0, stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, a.kv_len, a.num_splits, a.B, a.Hq, a.Hkv, a.S_cap, a.max_splits, c,
-                       a.part_o, a.part_lse);
+  const dim3 g((unsigned)grid), blk(64 * kWaves);
+  const bool fused = a.counters != nullptr;
+#define SA_LAUNCH(DD, FF)                                                                                   \
+  hipLaunchKernelGGL((decode_splitkv_bf16_kernel<DD, FF, kWaves>), g, blk, 0, stream, (const bf16*)a.q,    \
+                     (const bf16*)a.k, (const bf16*)a.v, a.kv_len, a.num_splits, a.B, a.Hq, a.Hkv, a.S_cap, \
+                     a.max_splits, c, a.part_o, a.part_lse, a.counters, (bf16*)a.o, a.lse)
+  if (a.d == 128) {
+    if (fused) SA_LAUNCH(128, true); else SA_LAUNCH(128, false);
+  } else {
+    if (fused) SA_LAUNCH(64, true); else SA_LAUNCH(64, false);
+  }
+#undef SA_LAUNCH
   return hipGetLastError();
 }
 

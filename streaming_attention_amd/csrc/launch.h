@@ -29,6 +29,10 @@ struct DecodeArgs {
   float scale;
   float* part_o;
   float* part_lse;
+  // Fused merge (attn_decode) when counters is non-null.
+  int32_t* counters;
+  void* o;
+  float* lse;
 };
 
 struct CombineArgs {

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_decode_splitkv", "attn_combine_lse", "attn_status_string"):
+    for n in ("attn_prefill", "attn_decode_splitkv", "attn_combine_lse", "attn_decode", "attn_status_string"):
         assert n in names
 
 
@@ -56,6 +56,22 @@ def decode(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=100, d=1
            dtype=BF16, scale=0.088, po=P, pl=P, stream=None):
     return sa.lib().attn_decode_splitkv(q, k, v, kv_len, ns, B, Hq, Hkv, S_cap, d, max_splits, dtype, scale,
                                         po, pl, stream)
+
+
+def decode_fused(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=100, d=128, max_splits=8,
+                 dtype=BF16, scale=0.088, po=P, pl=P, cnt=P, o=P, lse=P, stream=None):
+    return sa.lib().attn_decode(q, k, v, kv_len, ns, B, Hq, Hkv, S_cap, d, max_splits, dtype, scale,
+                                po, pl, cnt, o, lse, stream)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cnt=None), NULL), (dict(o=None), NULL), (dict(q=None), NULL), (dict(po=None), NULL),
+    (dict(max_splits=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(scale=-1.0), SHAPE),
+    (dict(dtype=F32), UNSUP), (dict(Hq=64, Hkv=2), UNSUP), (dict(cnt=MIS), ALIGN), (dict(o=MIS), ALIGN),
+    (dict(B=0), OK), (dict(B=0, cnt=None, o=None), OK),
+])
+def test_fused_decode_host_validation(kw, expect):
+    assert decode_fused(**kw) == expect
 
 
 def combine(po=P, pl=P, ns=None, B=2, Hq=8, max_splits=8, d=128, o=P, lse=P, dtype=BF16, stream=None):

@@ -61,7 +61,7 @@ def test_ragged_decode_full_size_nan_padding():
     w = W.RAGGED_DECODE
     q, k, v, lens = W.decode_inputs(w, DEV)
     ns = sa.splits_for_lengths(lens)
-    o, lse = sa.decode(q, k, v, lens.to(DEV), ns.to(DEV), max_splits=64, scale=w.scale)
+    o, lse = sa.decode(q, k, v, lens.to(DEV), ns.to(DEV), max_splits=64, scale=w.scale, fused=False)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     order = np.argsort(lens.numpy())
@@ -160,3 +160,56 @@ def test_decode_repeat_is_bitwise():
     o2, l2 = sa.decode(q, k, v, max_splits=16)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# attn_decode: split-KV + merge in one launch
+# ---------------------------------------------------------------------------
+
+def test_fused_decode_full_size_and_counters_reset():
+    """The 70B-shape decode through the fused entry point (the launch the bench
+    times), three calls in a row on one counter buffer."""
+    w = W.GQA70B_DECODE
+    q, k, v, lens = W.decode_inputs(w, DEV)
+    cnt = torch.zeros(w.B * w.Hkv, dtype=torch.int32, device=DEV)
+    for _ in range(3):
+        o, lse = sa.decode(q, k, v, None, None, max_splits=w.splits, scale=w.scale, counters=cnt, fused=True)
+    torch.cuda.synchronize()
+    assert int(cnt.abs().sum()) == 0, "counters must be zero after the launch"
+    _check_rows(o, lse, q, k, v, lens, w.scale, range(w.B))
+
+
+def test_fused_decode_ragged_nan_padding():
+    w = W.RAGGED_DECODE
+    q, k, v, lens = W.decode_inputs(w, DEV)
+    ns = sa.splits_for_lengths(lens)
+    o, lse = sa.decode(q, k, v, lens.to(DEV), ns.to(DEV), max_splits=64, scale=w.scale, fused=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    order = np.argsort(lens.numpy())
+    _check_rows(o, lse, q, k, v, lens, w.scale, sorted({int(order[0]), int(order[-1]), 5}))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S_cap,d,lens,nsplits,max_splits", SMALL)
+def test_fused_small_decode(B, Hq, Hkv, S_cap, d, lens, nsplits, max_splits):
+    g = torch.Generator(device=DEV).manual_seed(99 + S_cap + d)
+    q = torch.randn((B, Hq, 1, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    nt = torch.tensor(nsplits, dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(d)
+    o, lse = sa.decode(q, k, v, lt, nt, max_splits=max_splits, scale=scale, fused=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            assert (o[b].float() == 0).all() and torch.isneginf(lse[b]).all()
+            continue
+        O_ref, L_ref = oracle.decode_attention(f64(q[b:b + 1, :, 0]), f64(k[b:b + 1, :, :n]),
+                                               f64(v[b:b + 1, :, :n]), [n], scale)
+        assert_o(o[b, :, 0], O_ref[0], "bf16")
+        assert_lse(lse[b], L_ref[0], "bf16")
