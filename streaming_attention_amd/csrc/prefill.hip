@@ -11,9 +11,10 @@
 //
 // MI355X mapping (bf16 path)
 //   * One workgroup = 4 waves = 128 stacked query rows of one (batch, KV head);
-//     each wave owns 32 rows.  KV tiles of 64 keys are staged through LDS,
-//     double buffered, with the next tile's global loads in flight while the
-//     current tile is computed (one barrier per tile).
+//     each wave owns 32 rows.  KV tiles of 64 keys go from global memory
+//     straight into LDS (buffer loads with the LDS destination, no register
+//     staging), double buffered: the next tiles' loads are in flight while the
+//     current tile is computed, and one barrier per tile orders the rings.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     K (from LDS) is the A operand and Q (held in VGPRs for the whole sweep)
 //     the B operand.  In the accumulator layout every lane then owns ONE query
@@ -21,13 +22,12 @@
 //     holds the other 32.  Running max, running sum and the output rescale are
 //     therefore per-lane scalars, and a row reduction is a local reduction plus
 //     one exchange with the partner lane.
-//   * The output is accumulated transposed too, O^T += V^T P^T: V^T (from LDS)
-//     is the A operand, P^T the B operand.  The B operand of an MFMA needs, per
-//     lane, 8 consecutive reduction (key) indices of one query -- exactly 8
-//     consecutive accumulator registers of S^T, so P goes from the score
-//     accumulators to the P V operand with no data movement.  V is written to
-//     LDS transposed, with its key index permuted (bits 2 and 3 swapped) so that
-//     those 8 keys sit in 16 contiguous bytes of a V^T row.
+//   * The output is accumulated transposed too, O^T += V^T P^T: V^T is the A
+//     operand, P^T the B operand.  The B operand of an MFMA needs, per lane, 8
+//     reduction (key) indices of one query -- 8 accumulator registers of S^T,
+//     so P goes from the score accumulators to the P V operand with no data
+//     movement.  V stays row-major in LDS; the transposing LDS read of gfx950
+//     (ds_read_b64_tr_b16) delivers the matching V^T fragments.
 //   * Softmax runs in base 2: c = scale * log2(e) is folded into one FMA before
 //     v_exp_f32.  Masks are selects to -inf, never additions.
 //   * Work order: heaviest causal tiles first, and when the number of
@@ -37,6 +37,8 @@
 //
 // fp32 path: the same loop with v_mfma_f32_32x32x2_f32 (one K value per lane
 // per step, so V needs no transpose) and 32-key tiles, P kept in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -49,12 +51,6 @@ constexpr int kThreads = 256;
 constexpr int kNumCUs = 256;          // MI355X compute units
 constexpr float kRescaleLog2 = 8.f;   // lazy-rescale threshold (log2 units)
 constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
-
-// Permutation of a key index inside a 64-key tile for the V^T layout in LDS:
-// swap bits 2 and 3.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 struct TileCoord {
   int b, kvh, mt;
@@ -106,33 +102,74 @@ __device__ __forceinline__ void row_range_positions(int rA, int rB, int Sq, int&
 // ---------------------------------------------------------------------------
 // bf16 kernel
 //
+// LDS tiles.  A K or V tile is kBN key rows of D bf16 values, row-major (2 D
+// bytes a row, no padding), filled by direct global -> LDS buffer loads: one
+// such load stores the 16 bytes fetched by lane l at byte 16 l of a 1 KB
+// chunk, so which global bytes a lane fetches decides where they land.  Two
+// XOR swizzles, applied through that choice, keep the operand reads free of
+// bank conflicts:
+//   K  16-byte unit u of row r is stored at unit u ^ (r % U), U = D / 8.  The
+//      score A-operand read (32 consecutive rows, one unit each) then touches
+//      8 different units in every 8 consecutive rows.
+//   V  32-byte unit h of row r is stored at unit h ^ (r % 4).  The P V
+//      A-operand is read with ds_read_b64_tr_b16, whose 16-lane groups each
+//      read 4 rows x 32 bytes; those then fall on 4 different units.
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives
+// as its element e (e = 0..3) element i % 4 of the 8 bytes addressed by lane
+// 4 e + i / 4 of the group.  When the addressing lanes point at 4 consecutive
+// d values of 4 key rows, every lane receives one d column over 4 keys: the
+// transposed V operand, read straight from the row-major tile.
+//
 // QB = 32-row query blocks per wave (workgroup = 4 waves = 128 * QB stacked
 // rows).  QB = 2 halves the LDS bytes per MFMA (every K and V fragment read
-// from LDS feeds one MFMA per query block) at the cost of one wave per SIMD
-// (the output accumulators then live in AGPRs); QB = 1 runs two waves per SIMD
-// and suits problems with too few row tiles to fill the chip at QB = 2.
+// from LDS feeds one MFMA per query block) at the cost of one wave per SIMD.
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_t;
+
+__device__ __forceinline__ bf16x8 lds_read16(const lds_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+__device__ __forceinline__ s16x4 lds_read_tr16(const lds_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(p)));
+}
+// 16 bytes per lane, global (buffer, byte offset voff + soff) -> LDS chunk dst
+// (wave-uniform; lane l writes dst + 16 l).  Out-of-range bytes arrive as zero.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<__attribute__((address_space(3))) void*>(dst), 16,
+                                           voff, soff, 0, 0);
+}
+// Completion of this wave's direct-to-LDS loads (they count as vector memory
+// loads); a workgroup barrier after it publishes the tiles to all waves.
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int P>
+using Parity = std::integral_constant<int, P>;
+
 template <int D, bool CAUSAL, int QB>
 __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
     float c) {
-  constexpr int BM = 128 * QB;           // stacked query rows per workgroup
-  constexpr int RW = 32 * QB;            // rows per wave
-  constexpr int KP = D + 8;              // K tile row pitch (elements): 16 B pad
-  constexpr int VP = kBN + 8;            // V^T tile row pitch (elements): 16 B pad
-  constexpr int K_ELEMS = kBN * KP;
-  constexpr int V_ELEMS = D * VP;
-  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  constexpr int K_RPI = kThreads / CPR;  // K rows per load instruction
-  constexpr int NK = kBN / K_RPI;        // K loads per thread
-  constexpr int NV = kBN * CPR / kThreads;  // consecutive keys per thread for V (2 or 4)
-  constexpr int V_KG = kBN / NV;         // key groups per tile
-  constexpr int DS = D / 16;             // MFMA k-steps over d for S^T
-  constexpr int DB = D / 32;             // 32-row d blocks of O^T
-  static_assert(NV == 2 || NV == 4, "V staging assumes 2 or 4 keys per thread");
+  constexpr int BM = 128 * QB;              // stacked query rows per workgroup
+  constexpr int RW = 32 * QB;               // rows per wave
+  constexpr int RB = 2 * D;                 // bytes per K / V row
+  constexpr int U = D / 8;                  // 16-byte units per row
+  constexpr int TB = kBN * RB;              // bytes per tile
+  constexpr int NLD = kBN * U / kThreads;   // direct loads per thread per tile (4 or 2)
+  constexpr int DS = D / 16;                // MFMA k-steps over d for S^T
+  constexpr int DB = D / 32;                // 32-row d blocks of O^T
+  static_assert(NLD * kThreads == kBN * U, "a tile is a whole number of wave loads");
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * K_ELEMS + 2 * V_ELEMS];
+  // One array per ring slot: the compiler's wait-count analysis can then tell
+  // a direct load in flight into one slot from reads of another.
+  __shared__ __attribute__((aligned(1024))) char k_slot0[TB];
+  __shared__ __attribute__((aligned(1024))) char k_slot1[TB];
+  __shared__ __attribute__((aligned(1024))) char v_slot0[TB];
+  __shared__ __attribute__((aligned(1024))) char v_slot1[TB];
+  lds_t* const kbuf[2] = {(lds_t*)k_slot0, (lds_t*)k_slot1};
+  lds_t* const vbuf[2] = {(lds_t*)v_slot0, (lds_t*)v_slot1};
 
   const int G = Hq / Hkv;
   const int rows_total = G * Sq;
@@ -143,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   const int q_start = Skv - Sq;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int lr = l & 31;   // query column owned by this lane inside each row block
   const int hf = l >> 5;   // which half of the key set / d chunk the lane holds
@@ -151,8 +188,6 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   const size_t head0 = (size_t)tc.b * Hq + (size_t)tc.kvh * G;   // first query head of group
   const bf16* qg = q + head0 * Sq * D;
   const size_t kvoff = ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
-  const bf16* kg = k + kvoff;
-  const bf16* vg = v + kvoff;
 
   // This lane's query rows (one per row block) and their global positions.
   int row[QB], pos[QB];
@@ -187,70 +222,48 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     for (int s = 0; s < DS; ++s)
       qf[qb][s] = as_bf16x8(buf_ld16(rq, (uint32_t)row[qb] * D * 2 + 16 * hf + 32 * s, 0));
 
-  // Staging registers for one K tile and one V tile.
-  u32x4 kst[NK];
-  u32x4 vst[NV];
-  const int k_c = tid % CPR, k_rg = tid / CPR;
-  const int v_kg = tid % V_KG, v_c = tid / V_KG;
-
-  // K/V tiles come in through buffer loads over this (batch, KV head)'s rows:
-  // rows at or past Skv read as zero (their scores are masked to -inf, so P = 0
-  // and the zero V rows contribute nothing).  Per-lane offsets are fixed; the
-  // tile advances through the wave-uniform offset, so the loop spends no VALU
-  // on addresses, and unconditional loads stay in flight across a whole tile.
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (uint32_t)Skv * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (uint32_t)Skv * D * 2);
-  const uint32_t k_voff = (uint32_t)(k_rg * D + 8 * k_c) * 2;
-  const uint32_t v_voff = (uint32_t)(NV * v_kg * D + 8 * v_c) * 2;
-  auto load_k = [&](int kt) {
-    const uint32_t tile_off = (uint32_t)kt * kBN * D * 2;
+  // Direct loads: load j of this thread fills 16-byte unit p = 64 (4 j + w) + l
+  // of the tile, i.e. row p / U, stored unit p % U; the source offsets undo the
+  // swizzles.  Rows at or past Skv read as zero (their scores are masked to
+  // -inf, so P = 0, and the zero V rows add nothing).  The tile advances through
+  // the wave-uniform offset, so the loop spends no VALU on load addresses.
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Skv * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Skv * RB);
+  uint32_t k_src[NLD], v_src[NLD];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kst[i] = buf_ld16(rk, k_voff, tile_off + (uint32_t)(K_RPI * i * D * 2));
+  for (int j = 0; j < NLD; ++j) {
+    const int p = 64 * (4 * j + w) + l;
+    const int r = p / U, u = p % U;
+    k_src[j] = (uint32_t)(r * RB + 16 * (u ^ (r % U)));
+    v_src[j] = (uint32_t)(r * RB + 32 * ((u >> 1) ^ (r & 3)) + 16 * (u & 1));
+  }
+  auto load_k = [&](int kt, lds_t* dst) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) load_to_lds16(rk, dst + 1024 * (4 * j + w), k_src[j], (uint32_t)kt * TB);
   };
-  auto load_v = [&](int kt) {
-    const uint32_t tile_off = (uint32_t)kt * kBN * D * 2;
+  auto load_v = [&](int kt, lds_t* dst) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vst[i] = buf_ld16(rv, v_voff + (uint32_t)(i * D * 2), tile_off);
+    for (int j = 0; j < NLD; ++j) load_to_lds16(rv, dst + 1024 * (4 * j + w), v_src[j], (uint32_t)kt * TB);
   };
 
-  // LDS: a ring of two K tiles [key][d] and a ring of two V^T tiles [d][key'].
-  bf16* const Kring = smem;
-  bf16* const Vring = smem + 2 * K_ELEMS;
-  auto store_k = [&](int buf) {
-    bf16* Ks = Kring + buf * K_ELEMS;
+  // Operand read offsets.  Score A operand (K): row 32 kb + lr, logical unit
+  // 2 s + hf.  P V A operand (V^T, transposing read r of key chunk (kb, cc)):
+  // this lane addresses row 32 kb + 16 cc + 8 r + 4 (g / 2) + jj / 4 at
+  // d = 32 db + 16 (g % 2) + 4 (jj % 4), with g = l / 16, jj = l % 16, and so
+  // receives V[32 kb + 16 cc + 8 r + 4 hf + e][32 db + lr], e = 0..3: the keys
+  // of B-operand slots 4 r + e of P^T chunk (kb, cc) (see pack below).
+  uint32_t k_rd[DS];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) st16(Ks + (k_rg + K_RPI * i) * KP + 8 * k_c, kst[i]);
-  };
-  auto store_v = [&](int buf) {
-    // Transposed V: row d = 8 v_c + e holds the NV keys of this thread.
-    bf16* Vs = Vring + buf * V_ELEMS;
-    const int p0 = vt_pos(NV * v_kg);
+  for (int s = 0; s < DS; ++s) k_rd[s] = (uint32_t)(lr * RB + 16 * ((2 * s + hf) ^ (lr % U)));
+  const int g4 = l >> 4, jj = l & 15;
+  uint32_t v_rd[DB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16* dst = Vs + (8 * v_c + e) * VP + p0;
-      const int dw = e >> 1;
-      if constexpr (NV == 4) {
-        uint32_t a, bq;
-        if (e & 1) {
-          a = pack_hi(vst[0][dw], vst[1][dw]);
-          bq = pack_hi(vst[2][dw], vst[3][dw]);
-        } else {
-          a = pack_lo(vst[0][dw], vst[1][dw]);
-          bq = pack_lo(vst[2][dw], vst[3][dw]);
-        }
-        u32x2 pr = {a, bq};
-        *reinterpret_cast<u32x2*>(dst) = pr;
-      } else {
-        const uint32_t a = (e & 1) ? pack_hi(vst[0][dw], vst[1][dw]) : pack_lo(vst[0][dw], vst[1][dw]);
-        *reinterpret_cast<uint32_t*>(dst) = a;
-      }
-    }
-  };
+  for (int db = 0; db < DB; ++db)
+    v_rd[db] = (uint32_t)((4 * (g4 >> 1) + (jj >> 2)) * RB + 32 * ((2 * db + (g4 & 1)) ^ (jj >> 2)) + 8 * (jj & 3));
 
-  // S^T = K Q^T for the two 32-key blocks of the tile in K buffer `buf`, for
+  // S^T = K Q^T for the two 32-key blocks of the tile in K slot kb_lds, for
   // every row block: each K fragment read from LDS feeds QB MFMAs.
-  auto scores = [&](int buf, f32x16 (&S)[QB][2]) {
-    const bf16* Ks = Kring + buf * K_ELEMS;
+  auto scores = [&](const lds_t* Ks, f32x16 (&S)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -261,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     for (int s = 0; s < DS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + lr) * KP + 16 * s + 8 * hf);
+        const bf16x8 a = lds_read16(Ks + 32 * kb * RB + k_rd[s]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], S[qb][kb], 0, 0, 0);
@@ -291,16 +304,14 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   // mx were produced by the previous step:
   //   P1  mask (straddling / tail tiles only, then the max is recomputed) and
   //       the lazy-rescale decision;
-  //   P2  score MFMAs of tile kt + 1 (into Snext, from K buffer kbuf_next)
-  //       interleaved with this tile's exponentials and half of its bf16
-  //       packing;
-  //   P3  O^T += V^T P^T (V^T buffer vbuf) interleaved with the other half of
-  //       the packing, the row sums and the row max of tile kt + 1.
-  // After the last tile the score MFMAs run on an idle buffer and are
-  // discarded, which keeps them in the same basic block as the work they
-  // interleave with.
-  auto step = [&](int kt, f32x16 (&S)[QB][2], f32x16 (&Snext)[QB][2], float (&mx)[QB], int kbuf_next,
-                  int vbuf) {
+  //   P2  score MFMAs of tile kt + 1 (into Snext, from K slot Kn) interleaved
+  //       with this tile's exponentials and half of its bf16 packing;
+  //   P3  O^T += V^T P^T (V^T from V slot Vs) interleaved with the other half
+  //       of the packing, the row sums and the row max of tile kt + 1.
+  // After the last tile the score MFMAs run on an idle slot and are discarded,
+  // which keeps them in the same basic block as the work they interleave with.
+  auto step = [&](int kt, f32x16 (&S)[QB][2], f32x16 (&Snext)[QB][2], float (&mx)[QB], const lds_t* Kn,
+                  const lds_t* Vs) {
     const int key_end = kt * kBN + kBN - 1;
     const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
     if (need_mask) {
@@ -342,13 +353,15 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     // P2.  The wave raises its issue priority while it feeds the matrix core
     // (P2 + P3), so the arbiter prefers its MFMAs over the other wave's VALU.
     __builtin_amdgcn_s_setprio(1);
-    scores(kbuf_next, Snext);
+    scores(Kn, Snext);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[qb][kb][r] = exp2_hw(__builtin_fmaf(S[qb][kb][r], c, -m_use[qb]));
+    // P^T B operand of key chunk (kb, cc): accumulator registers 8 cc .. 8 cc + 7
+    // of block kb, i.e. slot e' holds key 32 kb + 16 cc + 8 (e' / 4) + 4 hf + e' % 4.
     bf16x8 pf[QB][2][2];
     auto pack = [&](int kb) {
 #pragma unroll
@@ -371,7 +384,6 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     }
 
     // P3.
-    const bf16* Vs = Vring + vbuf * V_ELEMS;
     pack(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -379,7 +391,9 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + (32 * db + lr) * VP + 32 * kb + 16 * cc + 8 * hf);
+          const lds_t* vp = Vs + (32 * kb + 16 * cc) * RB + v_rd[db];
+          const s16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * RB);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][cc], oacc[qb][db], 0, 0, 0);
@@ -389,48 +403,48 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
       l_run[qb] += sum_tree32(S[qb][0], S[qb][1]);
       mx[qb] = tile_max(Snext[qb]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLdsAhead, 0);
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // QB MFMAs
       __builtin_amdgcn_sched_group_barrier(0x002, 4 * QB, 0);   // 4 VALU each
-      if (i + kLdsAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
+      if (i + kLdsAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next two LDS reads
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
   // Software pipeline (the pages' "issue the next Q K^T before this tile's
-  // softmax"): K runs one tile ahead of V.  K tile kt + 2 and V tile kt + 1 are
-  // loaded during iteration kt and stored into the buffers that iteration
-  // kt - 1 finished reading; one barrier per tile orders the rings.
+  // softmax"): K runs one tile ahead of V.  Iteration kt (parity P = kt % 2)
+  // loads K tile kt + 2 into K slot P and V tile kt + 1 into V slot 1 - P --
+  // the slots iteration kt - 1 finished reading -- while it computes scores of
+  // tile kt + 1 from K slot 1 - P and the P V product of tile kt from V slot P.
+  // One barrier per tile, after this wave's loads have landed, orders the rings.
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
   wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
   f32x16 sA[QB][2], sB[QB][2];
   float mx[QB];
   if (n_tiles > 0) {
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-    load_k(1);
-    store_k(1);
+    load_k(0, kbuf[0]);
+    load_v(0, vbuf[0]);
+    load_k(1, kbuf[1]);
+    wait_lds_loads();
     __syncthreads();
-    scores(0, sA);
+    scores(kbuf[0], sA);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = tile_max(sA[qb]);
-    __syncthreads();   // K buffer 0 is rewritten in iteration 0
+    __syncthreads();   // K slot 0 is reloaded in iteration 0
   }
-  auto iteration = [&](int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
-    load_k(kt + 2);    // past the last tile these read zeros, stored into idle buffers
-    load_v(kt + 1);
-    step(kt, Scur, Snext, mx, (kt + 1) & 1, kt & 1);
-    store_k(kt & 1);
-    store_v((kt + 1) & 1);
+  auto iteration = [&](auto parity, int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
+    constexpr int P = decltype(parity)::value;
+    load_k(kt + 2, kbuf[P]);    // past the last tile these read zeros into idle slots
+    load_v(kt + 1, vbuf[1 - P]);
+    step(kt, Scur, Snext, mx, kbuf[1 - P], vbuf[P]);
+    wait_lds_loads();
     __syncthreads();
   };
   for (int kt = 0; kt < n_tiles; kt += 2) {
-    iteration(kt, sA, sB);
-    if (kt + 1 < n_tiles) iteration(kt + 1, sB, sA);
+    iteration(Parity<0>{}, kt, sA, sB);
+    if (kt + 1 < n_tiles) iteration(Parity<1>{}, kt + 1, sB, sA);
   }
 
   // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2.
