@@ -49,7 +49,8 @@ constexpr int kBM = 128;   // stacked query rows per workgroup (fp32 path)
 constexpr int kBN = 64;    // keys per KV tile (bf16 path)
 constexpr int kThreads = 256;
 constexpr int kNumCUs = 256;          // MI355X compute units
-constexpr float kRescaleLog2 = 8.f;   // lazy-rescale threshold (log2 units)
+constexpr float kSumCap = 16777216.f;  // 2^24: largest partial row sum of P accepted without
+                                      // raising the exponent base (P <= 2^24 keeps O far from fp32 overflow)
 constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
 
 struct TileCoord {
@@ -107,13 +108,16 @@ __device__ __forceinline__ void row_range_positions(int rA, int rB, int Sq, int&
 // such load stores the 16 bytes fetched by lane l at byte 16 l of a 1 KB
 // chunk, so which global bytes a lane fetches decides where they land.  Two
 // XOR swizzles, applied through that choice, keep the operand reads free of
-// bank conflicts:
-//   K  16-byte unit u of row r is stored at unit u ^ (r % U), U = D / 8.  The
-//      score A-operand read (32 consecutive rows, one unit each) then touches
-//      8 different units in every 8 consecutive rows.
-//   V  32-byte unit h of row r is stored at unit h ^ (r % 4).  The P V
-//      A-operand is read with ds_read_b64_tr_b16, whose 16-lane groups each
-//      read 4 rows x 32 bytes; those then fall on 4 different units.
+// bank conflicts on the 64 banks (256 bytes per clock) of the LDS:
+//   K  16-byte unit u of row r is stored at unit u ^ sk(r), with sk(r) = r % 16
+//      at D = 128 (256-byte rows) and (r / 2) % 8 at D = 64 (128-byte rows).
+//      The score A-operand read (rows 32 kb .. 32 kb + 31, one unit each,
+//      16 lanes per clock) then touches 16 different bank groups.
+//   V  32-byte unit h of row r is stored at unit h ^ sv(r), with
+//      sv(r) = 2 (r % 4) at D = 128 and 2 ((r / 2) % 2) at D = 64.  The P V
+//      A-operand is read with ds_read_b64_tr_b16; 32 lanes (two 16-lane
+//      groups) per clock read 4 rows x 2 adjacent 32-byte units, which then
+//      fall on 8 different units.
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives
 // as its element e (e = 0..3) element i % 4 of the 8 bytes addressed by lane
 // 4 e + i / 4 of the group.  When the addressing lanes point at 4 consecutive
@@ -161,6 +165,8 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   constexpr int DS = D / 16;                // MFMA k-steps over d for S^T
   constexpr int DB = D / 32;                // 32-row d blocks of O^T
   static_assert(NLD * kThreads == kBN * U, "a tile is a whole number of wave loads");
+  auto sk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto sv = [](int r) { return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); };
 
   // One array per ring slot: the compiler's wait-count analysis can then tell
   // a direct load in flight into one slot from reads of another.
@@ -234,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   for (int j = 0; j < NLD; ++j) {
     const int p = 64 * (4 * j + w) + l;
     const int r = p / U, u = p % U;
-    k_src[j] = (uint32_t)(r * RB + 16 * (u ^ (r % U)));
-    v_src[j] = (uint32_t)(r * RB + 32 * ((u >> 1) ^ (r & 3)) + 16 * (u & 1));
+    k_src[j] = (uint32_t)(r * RB + 16 * (u ^ sk(r)));
+    v_src[j] = (uint32_t)(r * RB + 32 * ((u >> 1) ^ sv(r)) + 16 * (u & 1));
   }
   auto load_k = [&](int kt, lds_t* dst) {
 #pragma unroll
@@ -254,33 +260,13 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   // of B-operand slots 4 r + e of P^T chunk (kb, cc) (see pack below).
   uint32_t k_rd[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) k_rd[s] = (uint32_t)(lr * RB + 16 * ((2 * s + hf) ^ (lr % U)));
+  for (int s = 0; s < DS; ++s) k_rd[s] = (uint32_t)(lr * RB + 16 * ((2 * s + hf) ^ sk(lr)));
   const int g4 = l >> 4, jj = l & 15;
+  const int vrow = 4 * (g4 >> 1) + (jj >> 2);   // row offset inside an 8-row read (chunk starts are multiples of 8)
   uint32_t v_rd[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-    v_rd[db] = (uint32_t)((4 * (g4 >> 1) + (jj >> 2)) * RB + 32 * ((2 * db + (g4 & 1)) ^ (jj >> 2)) + 8 * (jj & 3));
-
-  // S^T = K Q^T for the two 32-key blocks of the tile in K slot kb_lds, for
-  // every row block: each K fragment read from LDS feeds QB MFMAs.
-  auto scores = [&](const lds_t* Ks, f32x16 (&S)[QB][2]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) S[qb][kb][j] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = lds_read16(Ks + 32 * kb * RB + k_rd[s]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], S[qb][kb], 0, 0, 0);
-      }
-    }
-  };
+    v_rd[db] = (uint32_t)(vrow * RB + 32 * ((2 * db + (g4 & 1)) ^ sv(vrow)) + 8 * (jj & 3));
 
   // Running state per row block (per lane = per query row; l is this lane's
   // partial over its half of the keys).
@@ -300,151 +286,225 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   // partner lane that holds the other half of the tile's keys.
   auto tile_max = [&](const f32x16 (&S)[2]) { return max_xor32(max_of32(S[0], S[1])) * c; };
 
-  // One pipelined step for tile kt, whose scores S and unmasked scaled row max
-  // mx were produced by the previous step:
-  //   P1  mask (straddling / tail tiles only, then the max is recomputed) and
-  //       the lazy-rescale decision;
-  //   P2  score MFMAs of tile kt + 1 (into Snext, from K slot Kn) interleaved
-  //       with this tile's exponentials and half of its bf16 packing;
-  //   P3  O^T += V^T P^T (V^T from V slot Vs) interleaved with the other half
-  //       of the packing, the row sums and the row max of tile kt + 1.
-  // After the last tile the score MFMAs run on an idle slot and are discarded,
-  // which keeps them in the same basic block as the work they interleave with.
-  auto step = [&](int kt, f32x16 (&S)[QB][2], f32x16 (&Snext)[QB][2], float (&mx)[QB], const lds_t* Kn,
-                  const lds_t* Vs) {
-    const int key_end = kt * kBN + kBN - 1;
-    const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool vis = (key < Skv) && (!CAUSAL || key <= pos[qb]);
-            S[qb][kb][r] = vis ? S[qb][kb][r] : kNegInf;
-          }
-        mx[qb] = tile_max(S[qb]);
-      }
-    }
-    // Online softmax in base 2.  The running max used as the exponent base is
-    // only raised when a row's tile max exceeds it by more than kRescaleLog2
-    // (then O and l are rescaled); otherwise P may reach 2^kRescaleLog2, which
-    // fp32 and bf16 hold exactly enough.  O and l always share the same base,
-    // so O / l is unchanged (the rescale is skipped, not approximated).
-    float m_use[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const bool grow = mx[qb] > m_run[qb] + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx[qb] : m_run[qb];
-        const float corr = exp2_hw(m_run[qb] - m_new);   // 0 when m_run = -inf, 1 when unchanged
-        l_run[qb] *= corr;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[qb][i][j] *= corr;
-        m_run[qb] = m_new;
-      }
-      m_use[qb] = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
-    }
-
-    // P2.  The wave raises its issue priority while it feeds the matrix core
-    // (P2 + P3), so the arbiter prefers its MFMAs over the other wave's VALU.
-    __builtin_amdgcn_s_setprio(1);
-    scores(Kn, Snext);
+  // Online softmax in base 2 with a fixed exponent base.  The base m (per
+  // row) is the row max of the first tile; a later tile is exponentiated
+  // against the same m without computing its max: P = 2^(S c - m) may then
+  // exceed 1 (fp32 and bf16 keep their relative precision at any exponent),
+  // and O and l share the base, so O / l and LSE = (m + log2 l) ln 2 are
+  // unchanged.  Only when a row's partial sum of P over this lane's 32 keys
+  // exceeds kSumCap (so some P could be large enough to threaten fp32 range
+  // in O) is the tile redone: its scores are recomputed, its max taken, m
+  // raised, O and l rescaled by 2^(m_old - m_new) and P recomputed.  Data
+  // whose scores never climb far above the first tile's maximum never takes
+  // that path.
+  auto mask_tile = [&](int kt, f32x16 (&S)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[qb][kb][r] = exp2_hw(__builtin_fmaf(S[qb][kb][r], c, -m_use[qb]));
-    // P^T B operand of key chunk (kb, cc): accumulator registers 8 cc .. 8 cc + 7
-    // of block kb, i.e. slot e' holds key 32 kb + 16 cc + 8 (e' / 4) + 4 hf + e' % 4.
-    bf16x8 pf[QB][2][2];
-    auto pack = [&](int kb) {
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = (key < Skv) && (!CAUSAL || key <= pos[qb]);
+          S[qb][kb][r] = vis ? S[qb][kb][r] : kNegInf;
+        }
+  };
+  auto exponentiate = [&](f32x16 (&S)[QB][2], float (&psum)[QB]) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[qb][kb][r] = exp2_hw(__builtin_fmaf(S[qb][kb][r], c, -m_use));
+      psum[qb] = sum_tree32(S[qb][0], S[qb][1]);
+    }
+  };
+  auto raise_base = [&](const f32x16 (&S)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = fmaxf(m_run[qb], tile_max(S[qb]));
+      const float corr = (m_new == kNegInf) ? 1.f : exp2_hw(m_run[qb] - m_new);   // 0 from m = -inf
+      l_run[qb] *= corr;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[qb][i][j] *= corr;
+      m_run[qb] = m_new;
+    }
+  };
+  // P^T B operand of key chunk (kb, cc): P registers 8 cc .. 8 cc + 7 of block
+  // kb, i.e. slot e' holds key 32 kb + 16 cc + 8 (e' / 4) + 4 hf + e' % 4.
+  auto pack = [&](const f32x16 (&Pv)[QB][2], bf16x8 (&pf)[QB][2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const int r8 = 8 * cc;
-          pf[qb][kb][cc] = to_bf16x8(S[qb][kb][r8 + 0], S[qb][kb][r8 + 1], S[qb][kb][r8 + 2], S[qb][kb][r8 + 3],
-                                     S[qb][kb][r8 + 4], S[qb][kb][r8 + 5], S[qb][kb][r8 + 6], S[qb][kb][r8 + 7]);
+          pf[qb][kb][cc] = to_bf16x8(Pv[qb][kb][r8 + 0], Pv[qb][kb][r8 + 1], Pv[qb][kb][r8 + 2], Pv[qb][kb][r8 + 3],
+                                     Pv[qb][kb][r8 + 4], Pv[qb][kb][r8 + 5], Pv[qb][kb][r8 + 6], Pv[qb][kb][r8 + 7]);
         }
-    };
-    pack(0);
-    // Schedule: LDS reads run kLdsAhead fragments ahead of their MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+  };
+  // MFMA i (0..15) of the P V product of one tile: key chunk (i / 8, (i / 4) % 2)
+  // of V slot Vs, d block i % 4 (D = 128; D = 64 has 8 MFMAs, d block i % 2).
+  auto pv_mfma = [&](const lds_t* Vs, const bf16x8 (&pf)[QB][2][2], int i) {
+    const int kb = i / (2 * DB), cc = (i / DB) & 1, db = i % DB;
+    const lds_t* vp = Vs + (32 * kb + 16 * cc) * RB + v_rd[db];
+    const s16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * RB);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][cc], oacc[qb][db], 0, 0, 0);
+  };
+  // MFMA i (0 .. 2 DS - 1) of the scores of one tile: d step i / 2, key block i % 2.
+  auto score_mfma = [&](const lds_t* Ks, f32x16 (&S)[QB][2], int i) {
+    const int s = i >> 1, kb = i & 1;
+    const bf16x8 a = lds_read16(Ks + 32 * kb * RB + k_rd[s]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], S[qb][kb], 0, 0, 0);
+  };
+  // Rare path: the scores of tile kt again, with K read from global memory
+  // (its LDS slot is being refilled by then).
+  auto rescore_from_global = [&](int kt, f32x16 (&S)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) S[qb][kb][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = as_bf16x8(buf_ld16(rk, (uint32_t)((kt * kBN + 32 * kb + lr) * RB + 32 * s + 16 * hf), 0));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], S[qb][kb], 0, 0, 0);
+      }
+  };
+
+  // One pipelined step, three tiles deep:
+  //   P1  tile kt: mask (straddling / tail tiles only); on the first tile, m;
+  //   P2  the score MFMAs of tile kt + 1 (K slot Kn) and the P V MFMAs of tile
+  //       kt - 1 (V slot Vp, operand pf_prev) alternate, interleaved with the
+  //       exponentials, row sums and bf16 packing of tile kt;
+  //   P3  the range check of tile kt (rare redo), row sums into l.
+  // After the last tile the score MFMAs run on an idle slot and are discarded,
+  // which keeps them in the same basic block as the work they interleave with.
+  auto step = [&](int kt, f32x16 (&S)[QB][2], f32x16 (&Snext)[QB][2], const bf16x8 (&pf_prev)[QB][2][2],
+                  bf16x8 (&pf_new)[QB][2][2], const lds_t* Kn, const lds_t* Vp) {
+    const int key_end = kt * kBN + kBN - 1;
+    const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
+    if (need_mask) mask_tile(kt, S);
+    if (kt == 0) raise_base(S);   // O and l are still zero: this only sets m
+
+    // P2.  The wave raises its issue priority while it feeds the matrix core,
+    // so the arbiter prefers its MFMAs over the other wave's VALU.
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) Snext[qb][kb][j] = 0.f;
 #pragma unroll
     for (int i = 0; i < 2 * DS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);                  // QB MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x002, 5 * QB, 0);   // 5 VALU each
-      if (i + kLdsAhead < 2 * DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
+      score_mfma(Kn, Snext, i);
+      if (i < 4 * DB) pv_mfma(Vp, pf_prev, i);
     }
-
-    // P3.
-    pack(1);
+    float psum[QB];
+    exponentiate(S, psum);
+    pack(S, pf_new);
+    // Schedule: LDS reads run ahead of their MFMAs; ~3.5 VALU per MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kLdsAhead / 2, 0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const lds_t* vp = Vs + (32 * kb + 16 * cc) * RB + v_rd[db];
-          const s16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * RB);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][cc], oacc[qb][db], 0, 0, 0);
-        }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      l_run[qb] += sum_tree32(S[qb][0], S[qb][1]);
-      mx[qb] = tile_max(Snext[qb]);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLdsAhead, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // QB MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x002, 4 * QB, 0);   // 4 VALU each
-      if (i + kLdsAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next two LDS reads
+    for (int i = 0; i < 2 * DS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // score MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3 * QB, 0);   // VALU
+      if (i < 4 * DB) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // P V MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * QB, 0);   // VALU
+      }
+      if (2 * i + kLdsAhead < 4 * DS) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // next LDS reads
     }
     __builtin_amdgcn_s_setprio(0);
+
+    // P3.
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) over |= !(psum[qb] <= kSumCap);   // also catches inf / NaN
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      rescore_from_global(kt, S);
+      if (need_mask) mask_tile(kt, S);
+      raise_base(S);
+      exponentiate(S, psum);
+      pack(S, pf_new);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += psum[qb];
   };
 
   // Software pipeline (the pages' "issue the next Q K^T before this tile's
-  // softmax"): K runs one tile ahead of V.  Iteration kt (parity P = kt % 2)
-  // loads K tile kt + 2 into K slot P and V tile kt + 1 into V slot 1 - P --
-  // the slots iteration kt - 1 finished reading -- while it computes scores of
-  // tile kt + 1 from K slot 1 - P and the P V product of tile kt from V slot P.
-  // One barrier per tile, after this wave's loads have landed, orders the rings.
+  // softmax", one stage deeper): iteration kt (parity P = kt % 2) loads K tile
+  // kt + 2 into K slot P and V tile kt into V slot P -- slots iteration kt - 1
+  // finished reading -- while it computes the scores of tile kt + 1 from K
+  // slot 1 - P, the softmax of tile kt, and the P V product of tile kt - 1 from
+  // V slot 1 - P.  One barrier per tile, after this wave's loads have landed,
+  // orders the rings.  The P V product of the last tile follows the loop.
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
   wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
   f32x16 sA[QB][2], sB[QB][2];
-  float mx[QB];
+  bf16x8 pfA[QB][2][2], pfB[QB][2][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) pfB[qb][kb][cc] = bf16x8{};   // "tile -1": P = 0
   if (n_tiles > 0) {
     load_k(0, kbuf[0]);
-    load_v(0, vbuf[0]);
     load_k(1, kbuf[1]);
+    // V slot 1 plays tile -1 in iteration 0: zero it, so 0 * V stays 0.
+#pragma unroll
+    for (int i = 0; i < TB / (16 * kThreads); ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vbuf[1] + 16 * (tid + kThreads * i)) =
+          u32x4{0u, 0u, 0u, 0u};
     wait_lds_loads();
     __syncthreads();
-    scores(kbuf[0], sA);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = tile_max(sA[qb]);
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sA[qb][kb][j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2 * DS; ++i) score_mfma(kbuf[0], sA, i);
     __syncthreads();   // K slot 0 is reloaded in iteration 0
   }
-  auto iteration = [&](auto parity, int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
+  auto iteration = [&](auto parity, int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
+                       const bf16x8 (&pf_prev)[QB][2][2], bf16x8 (&pf_new)[QB][2][2]) {
     constexpr int P = decltype(parity)::value;
     load_k(kt + 2, kbuf[P]);    // past the last tile these read zeros into idle slots
-    load_v(kt + 1, vbuf[1 - P]);
-    step(kt, Scur, Snext, mx, kbuf[1 - P], vbuf[P]);
+    load_v(kt, vbuf[P]);
+    step(kt, Scur, Snext, pf_prev, pf_new, kbuf[1 - P], vbuf[1 - P]);
     wait_lds_loads();
     __syncthreads();
   };
   for (int kt = 0; kt < n_tiles; kt += 2) {
-    iteration(Parity<0>{}, kt, sA, sB);
-    if (kt + 1 < n_tiles) iteration(Parity<1>{}, kt + 1, sB, sA);
+    iteration(Parity<0>{}, kt, sA, sB, pfB, pfA);
+    if (kt + 1 < n_tiles) iteration(Parity<1>{}, kt + 1, sB, sA, pfA, pfB);
+  }
+  if (n_tiles > 0) {   // P V of the last tile: V slot and P registers by its parity
+    if (n_tiles & 1) {
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) pv_mfma(vbuf[0], pfA, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) pv_mfma(vbuf[1], pfB, i);
+    }
   }
 
   // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2.

@@ -211,3 +211,22 @@ def test_nan_after_the_last_key_row_is_never_read():
     v.copy_(torch.randn(shape, device=DEV).to(torch.bfloat16))
     q = torch.randn(1, 4, 70, 128, device=DEV).to(torch.bfloat16)
     run_and_check(q, k, v, causal=True)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("step", [2.0, 0.3, -1.0])
+def test_scores_that_climb_or_fall_across_tiles(step, causal, d):
+    """Key rows drift along the query direction by `step` per 64-key tile, so
+    the scores of later tiles rise far above (step 2.0: about 32 log2 units a
+    tile), gently above (0.3: the exponent base is raised only after several
+    tiles) or fall below (-1.0) the first tile's maximum.  Every kernel choice
+    of exponent base must still give the exact softmax."""
+    g = torch.Generator(device=DEV).manual_seed(int(100 * step) + d + causal)
+    Sq, Skv = 100, 600
+    q = (1.0 + 0.25 * torch.randn((1, 2, Sq, d), generator=g, device=DEV)).to(torch.bfloat16)
+    drift = step * (torch.arange(Skv, device=DEV) // 64).float()
+    k = (drift[None, None, :, None] + 0.25 * torch.randn((1, 1, Skv, d), generator=g, device=DEV)).to(torch.bfloat16)
+    v = torch.randn((1, 1, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    o, lse = run_and_check(q, k, v, causal)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
