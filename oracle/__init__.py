@@ -26,6 +26,7 @@ from .attn_f64 import (  # noqa: F401
     attention_rows,
     attention_online,
     partial_attention,
+    attention_key_range,
     merge_partials,
     decode_attention,
     visible_keys,

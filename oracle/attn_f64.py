@@ -201,6 +201,36 @@ def partial_attention(q, k, v, scale: float, key_lo: int, key_hi: int):
     return L, O
 
 
+def attention_key_range(q, k, v, scale: float, causal: bool, key_lo: int, key_hi: int):
+    """One split's result for every query row of a prefill: the definition with
+    only keys ``[key_lo, key_hi)`` (and, when causal, the usual diagonal mask)
+    visible.
+
+    On one device the pages' ring prefill ("ADR-0060", section 5.5: every step
+    folds one K/V block into the running state of each query block) and the
+    split partials of section 4 both reduce to this: each block of keys yields
+    a normalised pair ``(lse_i, O_i)`` for every query row, merged afterwards
+    by ``merge_partials``.  A row that sees no key of the range gives
+    ``(-inf, 0)``.
+
+    ``q [B,Hq,Sq,d]``, ``k, v [B,Hkv,Skv,d]``.  Returns ``O [B,Hq,Sq,d]`` and
+    ``LSE [B,Hq,Sq]`` (float64).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    vis = visible_keys(Sq, Skv, causal)
+    j = np.arange(Skv)
+    vis &= ((j >= key_lo) & (j < key_hi))[None, :]
+    O = np.zeros((B, Hq, Sq, v.shape[3]))
+    L = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            O[b, h], L[b, h] = _head(q[b, h], k[b, h // G], v[b, h // G], scale, vis)
+    return O, L
+
+
 def merge_partials(lse_parts, o_parts):
     """Combine partial results with the pages' log-sum-exp merge, float64.
 

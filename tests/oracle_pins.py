@@ -346,6 +346,49 @@ def check_partial_matches_restricted_definition(seed=10):
         _close(L, Lb[0, :, 0], 1e-12, f"partial LSE {lo}:{hi}")
 
 
+def check_key_range_partials(seed=11):
+    """Prefill partials over key ranges: brute force with the range cut out of
+    K and V (non-causal; causal via the shifted query block), the full range
+    equals the definition, and any partition merged by merge_partials gives
+    the full causal GQA result."""
+    r = _rng(seed)
+    B, Hq, Hkv, Sq, Skv, d = 1, 4, 2, 5, 9, 3
+    q = r.standard_normal((B, Hq, Sq, d))
+    k = r.standard_normal((B, Hkv, Skv, d))
+    v = r.standard_normal((B, Hkv, Skv, d))
+    for lo, hi in [(0, Skv), (2, 6), (8, 9), (5, 5)]:
+        O, L = oracle.attention_key_range(q, k, v, 0.7, False, lo, hi)
+        if hi <= lo:
+            assert np.all(np.isneginf(L)) and np.all(O == 0)
+            continue
+        Ob, Lb = brute_force(q.tolist(), k[:, :, lo:hi].tolist(), v[:, :, lo:hi].tolist(), 0.7, False)
+        _close(O, Ob, 1e-12, f"key range O {lo}:{hi}")
+        _close(L, Lb, 1e-12, f"key range LSE {lo}:{hi}")
+    # causal, range starting at 0: keys [0, hi) for a query block ending at hi
+    # is the ordinary causal attention of the rows whose positions are < hi
+    full = oracle.attention(q, k, v, 0.7, True)
+    same = oracle.attention_key_range(q, k, v, 0.7, True, 0, Skv)
+    _close(same[0], full[0], 1e-13, "causal full range O")
+    _close(same[1], full[1], 1e-13, "causal full range LSE")
+    hi, q_start = 6, Skv - Sq
+    part = oracle.attention_key_range(q, k, v, 0.7, True, 0, hi)
+    early = [t for t in range(Sq) if q_start + t < hi]    # all their visible keys lie in [0, hi)
+    late = [t for t in range(Sq) if q_start + t >= hi]    # they see exactly [0, hi)
+    assert early and late
+    _close(part[0][:, :, early], full[0][:, :, early], 1e-13, "causal prefix range O (early rows)")
+    _close(part[1][:, :, early], full[1][:, :, early], 1e-13, "causal prefix range LSE (early rows)")
+    Ob, Lb = brute_force(q[:, :, late].tolist(), k[:, :, :hi].tolist(), v[:, :, :hi].tolist(), 0.7, False)
+    _close(part[0][:, :, late], Ob, 1e-12, "causal prefix range O (late rows)")
+    _close(part[1][:, :, late], Lb, 1e-12, "causal prefix range LSE (late rows)")
+    for trial in range(6):
+        cuts = sorted(int(c) for c in r.integers(0, Skv + 1, int(r.integers(0, 5))))
+        bounds = [0] + cuts + [Skv]
+        parts = [oracle.attention_key_range(q, k, v, 0.7, True, a, b) for a, b in zip(bounds[:-1], bounds[1:])]
+        L, O = oracle.merge_partials(np.stack([p[1] for p in parts]), np.stack([p[0] for p in parts]))
+        _close(O, full[0], 1e-12, f"key range merge O trial {trial}")
+        _close(L, full[1], 1e-12, f"key range merge LSE trial {trial}")
+
+
 def check_empty_rows():
     """kv_len = 0 gives O = 0 and LSE = -inf."""
     q = np.ones((2, 2, 1, 3))
@@ -360,5 +403,5 @@ ALL_CHECKS = [
     check_brute_force, check_golden, check_golden_merge, check_zero_k, check_one_hot,
     check_ties, check_single_key, check_online_equals_two_pass, check_merge_any_partition,
     check_gqa_equals_repeated_mha, check_chunked_is_tail, check_scale_and_permutation,
-    check_partial_matches_restricted_definition, check_empty_rows,
+    check_partial_matches_restricted_definition, check_key_range_partials, check_empty_rows,
 ]

@@ -132,6 +132,17 @@ def _partial_off_by_one(q, k, v, scale, key_lo, key_hi):
 ORIG_PARTIAL = oa.partial_attention
 
 
+def _key_range_half_open_wrong(q, k, v, scale, causal, key_lo, key_hi):
+    return ORIG_KEY_RANGE(q, k, v, scale, causal, key_lo, key_hi + 1)   # mistake: range includes key_hi
+
+
+def _key_range_no_causal(q, k, v, scale, causal, key_lo, key_hi):
+    return ORIG_KEY_RANGE(q, k, v, scale, False, key_lo, key_hi)        # mistake: mask dropped
+
+
+ORIG_KEY_RANGE = oa.attention_key_range
+
+
 MUTATIONS = {
     "top_left_causal": ("visible_keys", _top_left_visible),
     "diagonal_hidden": ("visible_keys", _strict_diagonal),
@@ -142,6 +153,8 @@ MUTATIONS = {
     "online_no_rescale": ("attention_online", _online_no_rescale),
     "merge_wrong_sign": ("merge_partials", _merge_wrong_sign),
     "partial_off_by_one": ("partial_attention", _partial_off_by_one),
+    "key_range_inclusive_end": ("attention_key_range", _key_range_half_open_wrong),
+    "key_range_no_causal": ("attention_key_range", _key_range_no_causal),
 }
 
 
