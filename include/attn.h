@@ -6,6 +6,8 @@
  * O), so the score and probability matrices never reach memory:
  *
  *   attn_prefill         fused forward over a query block (GQA, causal or not)
+ *   attn_prefill_splitkv the same with the key range cut into splits, each
+ *                        yielding a partial result (merged by attn_combine_lse)
  *   attn_decode_splitkv  one query token per sequence, the KV range cut into
  *                        splits that each yield a partial result
  *   attn_combine_lse     merge of the split partials by log-sum-exp
@@ -91,13 +93,51 @@ enum {
  *
  * Sizes: B, Sq, Skv >= 0; Hq, Hkv >= 1 with Hq % Hkv == 0.  B == 0 or Sq == 0
  * is an empty call (returns ATTN_OK, enqueues nothing).  Skv == 0 (non-causal)
- * gives O = 0 and LSE = -inf.  k and v may be NULL when Skv == 0.
+ * gives O = 0 and LSE = -inf.  k and v may be NULL when Skv == 0.  The Q rows
+ * of one KV head (G * Sq * d elements) and the K or V rows of one (batch, KV
+ * head) (Skv * d elements) must each span less than 2 GiB.
  * Errors: ATTN_ERR_NULL (q, o, or k/v with Skv > 0), ATTN_ERR_SHAPE,
- * ATTN_ERR_UNSUPPORTED (d not 64/128, unknown dtype), ATTN_ERR_ALIGN.
+ * ATTN_ERR_UNSUPPORTED (d not 64/128, unknown dtype, a slice of 2 GiB or
+ * more), ATTN_ERR_ALIGN.
  */
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                  int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d,
                  int32_t dtype, int32_t causal, float scale, void* stream);
+
+/*
+ * attn_prefill_splitkv -- attn_prefill with the key range cut into splits, for
+ * query blocks too small to occupy the GPU (a short chunk of queries after a
+ * long prefix).  Every split yields a normalised partial result per query row;
+ * attn_combine_lse merges them.
+ *
+ * Defined by ADR-0060 section 5.5 (ring prefill: each step folds one K/V block
+ * into the running state of every query block; on one device the blocks
+ * become splits) and section 4 (each split's (m_i, l_i, O_i), merged by
+ * log-sum-exp), with the causal rules of attn_prefill.
+ *
+ *   q, k, v, B, Hq, Hkv, Sq, Skv, d, causal, scale   as for attn_prefill
+ *   dtype      ATTN_DTYPE_BF16 only
+ *   num_splits 1 .. 256
+ *   part_o     [B, Hq, Sq, num_splits, d] float32 (written)
+ *   part_lse   [B, Hq, Sq, num_splits]    float32 (written)
+ *
+ * Split plan (part of the contract): with T = ceil(Skv / 64) key tiles of 64
+ * and c = ceil(T / num_splits), split s covers keys [64 s c, min(64 (s + 1) c,
+ * Skv)).  part_lse[b,h,t,s] is the natural-log sum of exp of row t's visible
+ * scaled scores over that range and part_o[b,h,t,s,:] its attention output
+ * over that range alone; a row that sees no key of the range (or an empty
+ * range) gets (-inf, 0).  Every entry is written.
+ *
+ * The final result: attn_combine_lse(part_o, part_lse, NULL, B * Hq * Sq, 1,
+ * num_splits, d, o, lse, ATTN_DTYPE_BF16, stream) with o [B, Hq, Sq, d] and
+ * lse [B, Hq, Sq] -- the partial tensors are laid out as [rows, splits, ...]
+ * for exactly that call.
+ * Errors: as attn_prefill, plus ATTN_ERR_SHAPE (num_splits out of range) and
+ * ATTN_ERR_UNSUPPORTED (dtype other than bf16).
+ */
+int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* part_o, float* part_lse,
+                         int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d,
+                         int32_t num_splits, int32_t dtype, int32_t causal, float scale, void* stream);
 
 /*
  * attn_decode_splitkv -- one query token per sequence against a KV cache,

@@ -1,6 +1,7 @@
 """Streaming attention forward for AMD Instinct MI355X (gfx950).
 
-Fused prefill (GQA, causal), split-KV decode and the log-sum-exp combine, as
+Fused prefill (GQA, causal; split-KV for short query blocks after a long
+prefix), split-KV decode and the log-sum-exp combine, as
 hand-written HIP kernels behind the C ABI in ``include/attn.h``.  This package
 is the thin Python binding over ``libattn.so`` plus the seeded workloads.
 """
@@ -13,6 +14,8 @@ from ._binding import (  # noqa: F401
     decode_splitkv,
     lib,
     prefill,
+    prefill_splits,
+    prefill_splitkv,
     splits_for_lengths,
 )
 from . import workloads  # noqa: F401

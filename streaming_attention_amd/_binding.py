@@ -31,6 +31,7 @@ _F = ctypes.c_float
 
 SIGNATURES = {
     "attn_prefill": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P], ctypes.c_int),
+    "attn_prefill_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P], ctypes.c_int),
     "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], ctypes.c_int),
     "attn_combine_lse": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], ctypes.c_int),
     "attn_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P], ctypes.c_int),
@@ -95,14 +96,7 @@ def _check(status, where):
         raise AttnError(status, where)
 
 
-def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-            return_lse: bool = True):
-    """Fused streaming attention forward (``attn_prefill``).
-
-    ``q [B,Hq,Sq,d]``, ``k, v [B,Hkv,Skv,d]``, bf16 or fp32, contiguous, on one
-    GPU.  Causal alignment is bottom-right (the queries are the last Sq
-    positions).  Returns ``(o, lse)`` or ``o``.
-    """
+def _check_prefill_args(q, k, v):
     _need(q, "q", 4)
     dt = q.dtype
     if dt not in _DTYPE_CODE:
@@ -113,6 +107,69 @@ def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     Hkv, Skv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Hkv, Skv, d) or tuple(v.shape) != (B, Hkv, Skv, d):
         raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    return B, Hq, Hkv, Sq, Skv, d
+
+
+# Workgroups the prefill launch should reach to occupy the GPU: two per
+# compute unit of the MI355X (256 CUs), which is what the kernel's register
+# and LDS budget lets one CU hold.
+_PREFILL_WG_TARGET = 2 * 256
+
+
+def prefill_splits(B: int, Hq: int, Hkv: int, Sq: int, Skv: int, dtype=torch.bfloat16) -> int:
+    """KV splits for a prefill: 1 when the query blocks alone give enough
+    workgroups, else enough splits to reach the target, keeping at least 16
+    key tiles (1024 keys) per split.  A scheduling choice: any split count
+    gives the same result up to rounding."""
+    if dtype != torch.bfloat16:
+        return 1
+    blocks = -(-(Hq // Hkv) * Sq // 128) * B * Hkv
+    if blocks == 0 or blocks >= _PREFILL_WG_TARGET:
+        return 1
+    tiles = -(-Skv // 64)
+    return int(max(1, min(-(-_PREFILL_WG_TARGET // blocks), tiles // 16, 256)))
+
+
+def prefill_splitkv(q, k, v, num_splits: int, causal: bool = False, scale: float | None = None,
+                    part_o=None, part_lse=None):
+    """Split-KV prefill partials (``attn_prefill_splitkv``, bf16).
+
+    Returns ``(part_o [B,Hq,Sq,num_splits,d] f32, part_lse [B,Hq,Sq,num_splits] f32)``;
+    split ``s`` covers keys ``[64 s c, min(64 (s+1) c, Skv))`` with
+    ``c = ceil(ceil(Skv/64) / num_splits)``.
+    """
+    B, Hq, Hkv, Sq, Skv, d = _check_prefill_args(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("split-KV prefill takes bf16 inputs")
+    n = int(num_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if part_o is None:
+        part_o = torch.empty((B, Hq, Sq, n, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, Sq, n), dtype=torch.float32, device=q.device)
+    _need(part_o, "part_o", 5, torch.float32, q.device)
+    _need(part_lse, "part_lse", 4, torch.float32, q.device)
+    if tuple(part_o.shape) != (B, Hq, Sq, n, d) or tuple(part_lse.shape) != (B, Hq, Sq, n):
+        raise ValueError("partial buffers must be [B,Hq,Sq,num_splits,d] and [B,Hq,Sq,num_splits]")
+    st = lib().attn_prefill_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(part_o), _ptr(part_lse), B, Hq, Hkv, Sq,
+                                    Skv, d, n, ATTN_DTYPE_BF16, 1 if causal else 0, float(scale), _stream(q))
+    _check(st, "attn_prefill_splitkv")
+    return part_o, part_lse
+
+
+def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True, num_splits: int | None = None):
+    """Fused streaming attention forward.
+
+    ``q [B,Hq,Sq,d]``, ``k, v [B,Hkv,Skv,d]``, bf16 or fp32, contiguous, on one
+    GPU.  Causal alignment is bottom-right (the queries are the last Sq
+    positions).  ``num_splits`` None picks ``prefill_splits(...)``: 1 runs
+    ``attn_prefill``; more runs ``attn_prefill_splitkv`` and merges the
+    partials with ``attn_combine_lse`` (bf16 only).  Returns ``(o, lse)`` or ``o``.
+    """
+    B, Hq, Hkv, Sq, Skv, d = _check_prefill_args(q, k, v)
+    dt = q.dtype
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -127,9 +184,16 @@ def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         _need(lse, "lse", 3, torch.float32, q.device)
         if tuple(lse.shape) != (B, Hq, Sq):
             raise ValueError("lse must be [B,Hq,Sq]")
-    st = lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, d,
-                            _DTYPE_CODE[dt], 1 if causal else 0, float(scale), _stream(q))
-    _check(st, "attn_prefill")
+    n = prefill_splits(B, Hq, Hkv, Sq, Skv, dt) if num_splits is None else int(num_splits)
+    if n == 1:
+        st = lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, d,
+                                _DTYPE_CODE[dt], 1 if causal else 0, float(scale), _stream(q))
+        _check(st, "attn_prefill")
+    else:
+        po, pl = prefill_splitkv(q, k, v, n, causal, scale)
+        st = lib().attn_combine_lse(_ptr(po), _ptr(pl), None, B * Hq * Sq, 1, n, d, _ptr(out), _ptr(lse),
+                                    _DTYPE_CODE[dt], _stream(q))
+        _check(st, "attn_combine_lse")
     return (out, lse) if return_lse else out
 
 

@@ -14,6 +14,29 @@ constexpr long long kMaxGrid = (1LL << 24) - 1;   // workgroups per launch (x 25
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
+// Shared validation of attn_prefill / attn_prefill_splitkv.  Buffer offsets
+// inside one (batch, KV head) slice are 32-bit on the GPU, so each such slice
+// of Q, K and V must stay under 2 GiB.
+int check_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq,
+                  int32_t Skv, int32_t d, int32_t dtype, int32_t causal, float scale, long long n_splits) {
+  if (B < 0 || Sq < 0 || Skv < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (!good_scale(scale)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+  const long long G = Hq / Hkv;
+  if (G * (long long)Sq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const long long n_mt = (G * Sq + 127) / 128;
+  if (n_mt * (long long)B * Hkv * n_splits > kMaxGrid) return ATTN_ERR_SHAPE;
+  const long long esize = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+  if (G * Sq * d * esize > 0x7fffffffLL || (long long)Skv * d * esize > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (q == nullptr) return ATTN_ERR_NULL;
+  if (Skv > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || (Skv > 0 && (!aligned16(k) || !aligned16(v)))) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -33,20 +56,10 @@ const char* attn_status_string(int status) {
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                  int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d, int32_t dtype, int32_t causal, float scale,
                  void* stream) {
-  if (B < 0 || Sq < 0 || Skv < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
-  if (!good_scale(scale)) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
-  const long long G = Hq / Hkv;
-  if (G * (long long)Sq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  const long long n_mt = (G * Sq + 127) / 128;
-  if (n_mt * (long long)B * Hkv > kMaxGrid) return ATTN_ERR_SHAPE;
-  if (B == 0 || Sq == 0) return ATTN_OK;
-  if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
-  if (Skv > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv > 0 && (!aligned16(k) || !aligned16(v))))
-    return ATTN_ERR_ALIGN;
+  const int st = check_prefill(q, k, v, B, Hq, Hkv, Sq, Skv, d, dtype, causal, scale, 1);
+  if (st != ATTN_OK || B == 0 || Sq == 0) return st;
+  if (o == nullptr) return ATTN_ERR_NULL;
+  if (!aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
 
   sa::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -54,6 +67,27 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   a.bf16 = dtype == ATTN_DTYPE_BF16;
   a.causal = causal != 0;
   a.scale = scale;
+  return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* part_o, float* part_lse, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d, int32_t num_splits,
+                         int32_t dtype, int32_t causal, float scale, void* stream) {
+  if (num_splits < 1 || num_splits > 256) return ATTN_ERR_SHAPE;
+  const int st = check_prefill(q, k, v, B, Hq, Hkv, Sq, Skv, d, dtype, causal, scale, num_splits);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (part_o == nullptr || part_lse == nullptr) return ATTN_ERR_NULL;
+  if (!aligned16(part_o) || !aligned16(part_lse)) return ATTN_ERR_ALIGN;
+
+  sa::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = nullptr; a.lse = nullptr;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Skv = Skv; a.d = d;
+  a.bf16 = true;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.n_splits = num_splits; a.part_o = part_o; a.part_lse = part_lse;
   return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -8,11 +8,14 @@
 // merge is associative and commutative, so any grouping of the splits is a
 // valid merge order.
 //
-// MI355X mapping: one workgroup (4 waves) per (sequence, query head) row.  The
-// kernel is latency-bound (a few MB in total), so every load of a row is issued
-// in one round: the split lse values (one per thread, for the workgroup max M)
-// and, per wave, up to 16 partial rows (splits w, w + 4, ...; each lane owns
-// D / 64 output elements).  The four wave sums are added through LDS.
+// MI355X mapping.  Many splits (split-KV decode: tens of splits, few rows):
+// one workgroup (4 waves) per output row.  The kernel is latency-bound (a few
+// MB in total), so every load of a row is issued in one round: the split lse
+// values (one per thread, for the workgroup max M) and, per wave, up to 16
+// partial rows (splits w, w + 4, ...; each lane owns D / 64 output elements).
+// The four wave sums are added through LDS.  Few splits (at most kNarrow:
+// split-KV prefill, many rows): one wave per row, 4 rows per workgroup, every
+// lane reads the row's few lse values and its D / 64 elements of each partial.
 #include "common.h"
 #include "launch.h"
 
@@ -21,6 +24,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kUnroll = 16;
+constexpr int kNarrow = 8;   // largest split count handled one wave per row
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restrict__ part_o,
@@ -102,11 +106,73 @@ __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restric
   if (lse != nullptr && l == 0) lse[row] = ws > 0.f ? M + __logf(ws) : kNegInf;
 }
 
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_lse_narrow_kernel(const float* __restrict__ part_o,
+                                                                 const float* __restrict__ part_lse,
+                                                                 const int32_t* __restrict__ num_splits, int rows,
+                                                                 int Hq, int max_splits, void* __restrict__ o,
+                                                                 float* __restrict__ lse) {
+  constexpr int PER = D / 64;   // output elements per lane (consecutive)
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int l = threadIdx.x & 63;
+  int n = num_splits ? num_splits[row / Hq] : max_splits;
+  n = n < 1 ? 1 : (n > max_splits ? max_splits : n);
+  const float* L = part_lse + (size_t)row * max_splits;
+  const float* Op = part_o + (size_t)row * max_splits * D + PER * l;
+
+  float lv[kNarrow], ov[kNarrow][PER];
+#pragma unroll
+  for (int s = 0; s < kNarrow; ++s) {
+    lv[s] = s < n ? L[s] : kNegInf;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ov[s][i] = s < n ? Op[(size_t)s * D + i] : 0.f;
+  }
+  float M = lv[0];
+#pragma unroll
+  for (int s = 1; s < kNarrow; ++s) M = fmaxf(M, lv[s]);
+  const float Mb = (M == kNegInf) ? 0.f : M;   // all splits empty: every weight is exp2(-inf) = 0
+  float acc[PER], wsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kNarrow; ++s) {
+    const float wgt = exp2_hw((lv[s] - Mb) * kLog2e);
+    wsum += wgt;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += wgt * ov[s][i];
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = PER * l + i;
+    if (OUT_BF16)
+      reinterpret_cast<bf16*>(o)[(size_t)row * D + d] = (bf16)(acc[i] * inv);
+    else
+      reinterpret_cast<float*>(o)[(size_t)row * D + d] = acc[i] * inv;
+  }
+  if (lse != nullptr && l == 0) lse[row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+}
+
 }  // namespace
 
 hipError_t launch_combine_lse(const CombineArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.Hq;
-  const dim3 g((unsigned)rows), blk(256);
+  const dim3 blk(256);
+  if (a.max_splits <= kNarrow) {
+    const dim3 g((unsigned)((rows + kWaves - 1) / kWaves));
+#define SA_LAUNCH_N(DD, BF)                                                                                 \
+  hipLaunchKernelGGL((combine_lse_narrow_kernel<DD, BF>), g, blk, 0, stream, a.part_o, a.part_lse,         \
+                     a.num_splits, (int)rows, a.Hq, a.max_splits, a.o, a.lse)
+    if (a.d == 128) {
+      if (a.out_bf16) SA_LAUNCH_N(128, true); else SA_LAUNCH_N(128, false);
+    } else {
+      if (a.out_bf16) SA_LAUNCH_N(64, true); else SA_LAUNCH_N(64, false);
+    }
+#undef SA_LAUNCH_N
+    return hipGetLastError();
+  }
+  const dim3 g((unsigned)rows);
 #define SA_LAUNCH(DD, BF)                                                                                   \
   hipLaunchKernelGGL((combine_lse_kernel<DD, BF>), g, blk, 0, stream, a.part_o, a.part_lse, a.num_splits, a.B, \
                      a.Hq, a.max_splits, a.o, a.lse)

@@ -17,6 +17,11 @@ struct PrefillArgs {
   bool bf16;
   bool causal;
   float scale;
+  // Split-KV mode (bf16 only) when part_o is non-null: fp32 partials
+  // [B, Hq, Sq, n_splits, d] and [B, Hq, Sq, n_splits] instead of o / lse.
+  int n_splits = 1;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
 };
 
 struct DecodeArgs {

@@ -54,14 +54,15 @@ constexpr float kSumCap = 16777216.f;  // 2^24: largest partial row sum of P acc
 constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
 
 struct TileCoord {
-  int b, kvh, mt;
+  int b, kvh, mt, split;
 };
 
-// Workgroup index -> (batch, KV head, M tile).  Heaviest M tiles (latest query
-// positions) are dealt first; with n_groups % 8 == 0 each group is pinned to
-// XCD (group % 8).
+// Workgroup index -> (batch, KV head, KV split, M tile).  A (batch, KV head,
+// split) triple is a "group" here.  Heaviest M tiles (latest query positions)
+// are dealt first; with n_groups % 8 == 0 each group is pinned to XCD
+// (group % 8), so the workgroups that stream the same K/V range share an L2.
 template <int BM>
-__device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int Hkv, int n_mt, int G,
+__device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int n_splits, int Hkv, int n_mt, int G,
                                               int Sq) {
   int group, rk;
   if ((n_groups & 7) == 0) {
@@ -82,6 +83,8 @@ __device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int Hkv, int
     mt = n_mt - 1 - rk;
   }
   TileCoord t;
+  t.split = group % n_splits;
+  group /= n_splits;
   t.b = group / Hkv;
   t.kvh = group % Hkv;
   t.mt = mt;
@@ -151,11 +154,16 @@ __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt
 template <int P>
 using Parity = std::integral_constant<int, P>;
 
+//
+// Split-KV mode (part_o != nullptr): the workgroup covers only KV split
+// tc.split -- tiles [s T, min((s + 1) T, all tiles)) with T = ceil(tiles /
+// n_splits), intersected with the causal extent -- and writes the normalised
+// fp32 partial (O over those keys, their LSE) in place of O and LSE.
 template <int D, bool CAUSAL, int QB>
 __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
-    float c) {
+    float c, int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int BM = 128 * QB;              // stacked query rows per workgroup
   constexpr int RW = 32 * QB;               // rows per wave
   constexpr int RB = 2 * D;                 // bytes per K / V row
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   const int rows_total = G * Sq;
   const int n_mt = (rows_total + BM - 1) / BM;
   const int n_groups = B * Hkv;
-  const TileCoord tc = map_tile<BM>(blockIdx.x, n_groups, Hkv, n_mt, G, Sq);
+  const TileCoord tc = map_tile<BM>(blockIdx.x, n_groups * n_splits, n_splits, Hkv, n_mt, G, Sq);
   const int r0 = tc.mt * BM;
   const int q_start = Skv - Sq;
 
@@ -203,13 +211,17 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     pos[qb] = q_start + (row[qb] < rows_total ? row[qb] % Sq : 0);
   }
 
-  // Causal extents: loop bound for the workgroup, mask-free bound per wave.
-  int n_tiles = (Skv + kBN - 1) / kBN;
+  // Tile range of this workgroup (its KV split, cut at the causal extent) and
+  // the mask-free bound per wave.
+  const int tiles_all = (Skv + kBN - 1) / kBN;
+  const int tiles_per_split = (tiles_all + n_splits - 1) / n_splits;
+  int kt_lo = tc.split * tiles_per_split;
+  int kt_hi = min(tiles_all, kt_lo + tiles_per_split);
   int wave_tmin = 0x3fffffff;
   if (CAUSAL) {
     int tmin, tmax;
     row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, tmin, tmax);
-    n_tiles = min(n_tiles, (q_start + tmax) / kBN + 1);
+    kt_hi = min(kt_hi, (q_start + tmax) / kBN + 1);
     const int wA = r0 + RW * w, wB = min(r0 + RW * w + RW - 1, rows_total - 1);
     if (wA <= wB) {
       int a, bb;
@@ -399,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     const int key_end = kt * kBN + kBN - 1;
     const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
     if (need_mask) mask_tile(kt, S);
-    if (kt == 0) raise_base(S);   // O and l are still zero: this only sets m
+    if (kt == kt_lo) raise_base(S);   // O and l are still zero: this only sets m
 
     // P2.  The wave raises its issue priority while it feeds the matrix core,
     // so the arbiter prefers its MFMAs over the other wave's VALU.
@@ -454,7 +466,8 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   // slot 1 - P, the softmax of tile kt, and the P V product of tile kt - 1 from
   // V slot 1 - P.  One barrier per tile, after this wave's loads have landed,
   // orders the rings.  The P V product of the last tile follows the loop.
-  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+  kt_lo = __builtin_amdgcn_readfirstlane(kt_lo);
+  kt_hi = __builtin_amdgcn_readfirstlane(kt_hi);
   wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
   f32x16 sA[QB][2], sB[QB][2];
   bf16x8 pfA[QB][2][2], pfB[QB][2][2];
@@ -464,9 +477,9 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) pfB[qb][kb][cc] = bf16x8{};   // "tile -1": P = 0
-  if (n_tiles > 0) {
-    load_k(0, kbuf[0]);
-    load_k(1, kbuf[1]);
+  if (kt_hi > kt_lo) {
+    load_k(kt_lo, kbuf[0]);
+    load_k(kt_lo + 1, kbuf[1]);
     // V slot 1 plays tile -1 in iteration 0: zero it, so 0 * V stays 0.
 #pragma unroll
     for (int i = 0; i < TB / (16 * kThreads); ++i)
@@ -487,18 +500,18 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   auto iteration = [&](auto parity, int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
                        const bf16x8 (&pf_prev)[QB][2][2], bf16x8 (&pf_new)[QB][2][2]) {
     constexpr int P = decltype(parity)::value;
-    load_k(kt + 2, kbuf[P]);    // past the last tile these read zeros into idle slots
+    load_k(kt + 2, kbuf[P]);    // past the range these fill idle slots (zeros past Skv)
     load_v(kt, vbuf[P]);
     step(kt, Scur, Snext, pf_prev, pf_new, kbuf[1 - P], vbuf[1 - P]);
     wait_lds_loads();
     __syncthreads();
   };
-  for (int kt = 0; kt < n_tiles; kt += 2) {
+  for (int kt = kt_lo; kt < kt_hi; kt += 2) {
     iteration(Parity<0>{}, kt, sA, sB, pfB, pfA);
-    if (kt + 1 < n_tiles) iteration(Parity<1>{}, kt + 1, sB, sA, pfA, pfB);
+    if (kt + 1 < kt_hi) iteration(Parity<1>{}, kt + 1, sB, sA, pfA, pfB);
   }
-  if (n_tiles > 0) {   // P V of the last tile: V slot and P registers by its parity
-    if (n_tiles & 1) {
+  if (kt_hi > kt_lo) {   // P V of the last tile: V slot and P registers by its parity
+    if ((kt_hi - kt_lo) & 1) {
 #pragma unroll
       for (int i = 0; i < 4 * DB; ++i) pv_mfma(vbuf[0], pfA, i);
     } else {
@@ -507,27 +520,44 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     }
   }
 
-  // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2.
+  // Epilogue: O = O^T / l per row, LSE = (m + log2 l) ln 2; in split-KV mode
+  // the same pair in fp32 into this split's partial slot.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = sum_xor32(l_run[qb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_row = l_tot > 0.f ? (m_run[qb] + __log2f(l_tot)) * kLn2 : kNegInf;
     if (row[qb] < rows_total) {
-      bf16* orow = o + (head0 * Sq + row[qb]) * D;
+      const size_t flat = head0 * Sq + row[qb];   // row of [B, Hq, Sq]
+      if (part_o != nullptr) {
+        const size_t slot = flat * n_splits + tc.split;
+        float* prow = part_o + slot * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * db + 8 * q4 + 4 * hf;
-          const uint32_t lo = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 0] * inv)),
-                                      __builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 1] * inv)));
-          const uint32_t hi = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 2] * inv)),
-                                      __builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 3] * inv)));
-          u32x2 pr = {lo, hi};
-          *reinterpret_cast<u32x2*>(orow + d0) = pr;
-        }
-      if (lse != nullptr && hf == 0)
-        lse[head0 * Sq + row[qb]] = l_tot > 0.f ? (m_run[qb] + __log2f(l_tot)) * kLn2 : kNegInf;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * db + 8 * q4 + 4 * hf;
+            f32x4 val = {oacc[qb][db][4 * q4 + 0] * inv, oacc[qb][db][4 * q4 + 1] * inv,
+                         oacc[qb][db][4 * q4 + 2] * inv, oacc[qb][db][4 * q4 + 3] * inv};
+            *reinterpret_cast<f32x4*>(prow + d0) = val;
+          }
+        if (hf == 0) part_lse[slot] = lse_row;
+      } else {
+        bf16* orow = o + flat * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * db + 8 * q4 + 4 * hf;
+            const uint32_t lo = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 0] * inv)),
+                                        __builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 1] * inv)));
+            const uint32_t hi = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 2] * inv)),
+                                        __builtin_bit_cast(uint16_t, (bf16)(oacc[qb][db][4 * q4 + 3] * inv)));
+            u32x2 pr = {lo, hi};
+            *reinterpret_cast<u32x2*>(orow + d0) = pr;
+          }
+        if (lse != nullptr && hf == 0) lse[flat] = lse_row;
+      }
     }
   }
 }
@@ -556,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
   const int G = Hq / Hkv;
   const int rows_total = G * Sq;
   const int n_mt = (rows_total + kBM - 1) / kBM;
-  const TileCoord tc = map_tile<kBM>(blockIdx.x, B * Hkv, Hkv, n_mt, G, Sq);
+  const TileCoord tc = map_tile<kBM>(blockIdx.x, B * Hkv, 1, Hkv, n_mt, G, Sq);
   const int r0 = tc.mt * kBM;
   const int q_start = Skv - Sq;
 
@@ -705,11 +735,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     // MFMA but, at one wave per SIMD, measured slower on the 70B-shape prefill:
     // 756 vs 941 TFLOP/s, the compiler shuttling accumulators between AGPRs
     // and VGPRs.)
-    const dim3 g((unsigned)((rows + 127) / 128 * groups));
+    const dim3 g((unsigned)((rows + 127) / 128 * groups * a.n_splits));
 #define SA_LAUNCH_BF16(DD, CC, QQ)                                                                      \
   hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, QQ>), g, blk, 0, stream, (const bf16*)a.q,          \
                      (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,     \
-                     a.Skv, c)
+                     a.Skv, c, a.n_splits, a.part_o, a.part_lse)
     if (a.d == 128) {
       if (a.causal) {
         SA_LAUNCH_BF16(128, true, 1);

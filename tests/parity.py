@@ -71,3 +71,11 @@ def split_bounds(length: int, n: int, granule: int = 64):
         hi = min((s + 1) * chunk, length)
         out.append((lo, hi))
     return out
+
+
+def prefill_split_bounds(Skv: int, n: int, tile: int = 64):
+    """Key ranges of the split-KV prefill plan stated in include/attn.h:
+    T = ceil(Skv / tile) tiles, c = ceil(T / n) tiles per split."""
+    T = -(-Skv // tile)
+    c = -(-T // n) if T > 0 else 0
+    return [(min(tile * s * c, Skv), min(tile * (s + 1) * c, Skv)) for s in range(n)]

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_decode_splitkv", "attn_combine_lse", "attn_decode", "attn_status_string"):
+    for n in ("attn_prefill", "attn_prefill_splitkv", "attn_decode_splitkv", "attn_combine_lse", "attn_decode",
+              "attn_status_string"):
         assert n in names
 
 
@@ -50,6 +51,24 @@ def test_status_strings():
 def prefill(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, Sq=16, Skv=32, d=128, dtype=BF16, causal=1,
             scale=0.088, stream=None):
     return sa.lib().attn_prefill(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, dtype, causal, scale, stream)
+
+
+def prefill_split(q=P, k=P, v=P, po=P, pl=P, B=1, Hq=8, Hkv=2, Sq=16, Skv=32, d=128, n=4, dtype=BF16, causal=1,
+                  scale=0.088, stream=None):
+    return sa.lib().attn_prefill_splitkv(q, k, v, po, pl, B, Hq, Hkv, Sq, Skv, d, n, dtype, causal, scale, stream)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), NULL), (dict(po=None), NULL), (dict(pl=None), NULL), (dict(k=None), NULL),
+    (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(Sq=40, Skv=32), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(q=MIS), ALIGN), (dict(po=MIS), ALIGN), (dict(pl=MIS), ALIGN), (dict(v=MIS), ALIGN),
+    (dict(B=0), OK), (dict(Sq=0), OK), (dict(B=0, q=None, po=None, pl=None), OK),
+    (dict(Hq=64, Hkv=8, Sq=1 << 20, Skv=1 << 20, B=64, n=64), SHAPE),
+    (dict(Skv=1 << 23, Sq=16, n=1), UNSUP),   # K/V slice of one KV head >= 2 GiB
+])
+def test_prefill_splitkv_host_validation(kw, expect):
+    assert prefill_split(**kw) == expect
 
 
 def decode(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=100, d=128, max_splits=8,
@@ -87,6 +106,7 @@ def combine(po=P, pl=P, ns=None, B=2, Hq=8, max_splits=8, d=128, o=P, lse=P, dty
     (dict(q=MIS), ALIGN), (dict(k=MIS), ALIGN), (dict(o=MIS), ALIGN), (dict(lse=MIS), ALIGN),
     (dict(B=0), OK), (dict(Sq=0), OK), (dict(B=0, q=None, o=None), OK),
     (dict(Hq=64, Hkv=8, Sq=1 << 28, Skv=1 << 28, B=64), SHAPE),
+    (dict(Skv=1 << 23, Sq=16), UNSUP), (dict(Hq=64, Hkv=1, Sq=1 << 17, Skv=1 << 17), UNSUP),
 ])
 def test_prefill_host_validation(kw, expect):
     assert prefill(**kw) == expect
@@ -128,6 +148,14 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.lib()
+
+
+def test_prefill_splits_heuristic():
+    assert sa.prefill_splits(1, 64, 8, 512, 66048) == 2        # 256 query blocks after a 64K prefix
+    assert sa.prefill_splits(1, 64, 8, 8192, 8192) == 1        # 4096 blocks already
+    assert sa.prefill_splits(1, 64, 8, 512, 66048, torch.float32) == 1
+    assert sa.prefill_splits(1, 8, 8, 64, 1 << 20) == 64       # few rows, long prefix: 8 blocks x 64
+    assert sa.prefill_splits(1, 8, 1, 200, 333) == 1           # too few key tiles to split
 
 
 def test_splits_for_lengths():

@@ -9,7 +9,7 @@ import torch
 import oracle
 import streaming_attention_amd as sa
 from streaming_attention_amd import workloads as W
-from parity import assert_lse, assert_o, assert_rel_fro, f64
+from parity import assert_lse, assert_o, assert_rel_fro, f64, prefill_split_bounds
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -230,3 +230,69 @@ def test_scores_that_climb_or_fall_across_tiles(step, causal, d):
     v = torch.randn((1, 1, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
     o, lse = run_and_check(q, k, v, causal)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+
+# Split-KV prefill: every split's partial against the definition restricted to
+# its key range, and the merged result against the whole definition.  Cases:
+# GQA causal chunk after a prefix, non-causal d = 64, many splits of a short
+# query block, more splits than tiles (empty splits), a single query row.
+SPLIT = [
+    # B, Hq, Hkv, Sq, Skv, d, causal, n
+    (1, 8, 2, 130, 700, 128, True, 3),
+    (2, 4, 4, 64, 333, 64, False, 4),
+    (1, 16, 2, 40, 1000, 128, True, 7),
+    (1, 2, 1, 16, 100, 128, True, 5),
+    (1, 8, 8, 1, 257, 128, True, 2),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal,n", SPLIT)
+def test_split_prefill_partials_and_merge(B, Hq, Hkv, Sq, Skv, d, causal, n):
+    g = torch.Generator(device=DEV).manual_seed(2000 + Sq + Skv + n)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    po, pl = sa.prefill_splitkv(q, k, v, n, causal=causal, scale=scale)
+    o, lse = sa.prefill(q, k, v, causal=causal, scale=scale, num_splits=n)
+    torch.cuda.synchronize()
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    for s, (lo, hi) in enumerate(prefill_split_bounds(Skv, n)):
+        O_s, L_s = oracle.attention_key_range(qf, kf, vf, scale, causal, lo, hi)
+        assert_o(po[:, :, :, s], O_s, "bf16", f"partial O split {s} [{lo},{hi})")
+        assert_lse(pl[:, :, :, s], L_s, "bf16", f"partial LSE split {s} [{lo},{hi})")
+    O_ref, L_ref = oracle.attention(qf, kf, vf, scale, causal)
+    assert_o(o, O_ref, "bf16")
+    assert_lse(lse, L_ref, "bf16")
+    assert_rel_fro(o, O_ref)
+
+
+def test_split_prefill_without_keys_gives_zero_and_neg_inf():
+    q = torch.randn(1, 4, 8, 128, device=DEV).to(torch.bfloat16)
+    k = torch.empty(1, 2, 0, 128, device=DEV, dtype=torch.bfloat16)
+    po, pl = sa.prefill_splitkv(q, k, k, 3, causal=False)
+    o, lse = sa.prefill(q, k, k, causal=False, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.all(po == 0) and torch.all(torch.isneginf(pl))
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_split_prefill_matches_unsplit_on_the_chunked_shape_rows():
+    """512 queries after a 65536-key prefix (64 / 8 heads, d = 128): the
+    automatic choice splits the keys in two; sampled rows of that result and
+    of the unsplit kernel both meet the bar against the oracle."""
+    w = W.CHUNKED_PREFILL
+    assert sa.prefill_splits(w.B, w.Hq, w.Hkv, w.Sq, w.Skv) == 2
+    q, k, v = W.prefill_inputs(w, DEV)
+    o2, l2 = sa.prefill(q, k, v, causal=True, scale=w.scale)
+    o1, l1 = sa.prefill(q, k, v, causal=True, scale=w.scale, num_splits=1)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 510, 511]
+    for h in (0, 9, 63):
+        kvh = h // (w.Hq // w.Hkv)
+        O_ref, L_ref = oracle.attention_rows(f64(q[:, h:h + 1]), f64(k[:, kvh:kvh + 1]), f64(v[:, kvh:kvh + 1]),
+                                             w.scale, True, 0, 0, rows)
+        for o, l in ((o1, l1), (o2, l2)):
+            assert_o(o[0, h, rows], O_ref, "bf16")
+            assert_lse(l[0, h, rows], L_ref, "bf16")
