@@ -10,7 +10,9 @@ One step = one pass of the whole path on resident synthetic inputs:
 Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s
 (4 * d * visible (q, k) pairs per head / prefill kernel time); the decode
 throughput in KV GB/s (every valid K and V byte once / split + combine time)
-is reported next to it.  Kernel times come from HIP events recorded on the
+is reported next to it.  Outside the step, the chunked prefill (512 queries
+after a 65536-token prefix, split-KV + merge) is timed on its own and reported
+as `chunked_prefill`.  Kernel times come from HIP events recorded on the
 stream the kernels run on, over the timed steps.  The float64 oracle, timed on
 the host cores on a bounded sample of the same prefill workload, is reported as
 `cpu_baseline` (a baseline only).
@@ -39,14 +41,16 @@ METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQ
 # (`bench.py --only copy`: FETCH_SIZE reads 0.5x the copied bytes, WRITE_SIZE 1.0x).
 # Each entry holds for the kernel sources whose hash it records; after any change to
 # them the bench reports traffic as null until the counters are taken again.
-# Summary and commands: profiles/gqa70b_hbm_traffic.md.
+# Summary and commands: profiles/hbm_traffic_70b_prefill_decode_chunked.md.
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "7cdc64eee1e3970c",
-                "fetch_kib": 162340, "write_kib": 133213},
-    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "stale",
-               "fetch_kib": 0, "write_kib": 0},
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "bf17bc2bf59fe0c8",
+                "fetch_kib": 146992, "write_kib": 133123},
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "81d7970cf0f2d9a1",
+               "fetch_kib": 262478 + 4172, "write_kib": 8704 + 72},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "8bab83e9653b1752",
+                "fetch_kib": 250896 + 16917, "write_kib": 33280 + 8448},
 }
 
 
@@ -69,9 +73,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
-                    help="run only one half of the step (for per-kernel profiling runs); 'copy' runs a "
-                         "plain 1 GiB device copy, the reference for scaling HBM byte counters")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "chunked", "copy"], default="all",
+                    help="run only one part (for per-kernel profiling runs): one half of the step, the "
+                         "chunked prefill, or 'copy', a plain 1 GiB device copy that is the reference for "
+                         "scaling HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -163,6 +168,7 @@ def main():
 
     do_pf = args.only in ("all", "prefill")
     do_dc = args.only in ("all", "decode")
+    do_ch = args.only in ("all", "chunked")
 
     def step(i=None):
         if i is not None:
@@ -177,18 +183,50 @@ def main():
         if i is not None:
             ev[i][2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = 0.0
+    if do_pf or do_dc:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
-    pf_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)) / n_ev
-    dc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)) / n_ev
+    pf_ms = dc_ms = float("nan")
+    if do_pf or do_dc:
+        pf_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)) / n_ev
+        dc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)) / n_ev
     ms_step = wall * 1e3 / args.steps
+
+    chunked = None
+    if do_ch:   # split-KV prefill + merge, timed on its own (not part of the step)
+        wc = W.CHUNKED_PREFILL
+        qc, kc2, vc2 = W.prefill_inputs(wc, dev)
+        oc = torch.empty_like(qc)
+        lsec = torch.empty((wc.B, wc.Hq, wc.Sq), dtype=torch.float32, device=dev)
+        n_sp = sa.prefill_splits(wc.B, wc.Hq, wc.Hkv, wc.Sq, wc.Skv)
+        for _ in range(args.warmup):
+            sa.prefill(qc, kc2, vc2, causal=True, scale=wc.scale, out=oc, lse=lsec)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            sa.prefill(qc, kc2, vc2, causal=True, scale=wc.scale, out=oc, lse=lsec)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ch_ms = e0.elapsed_time(e1) / args.steps
+        ch_tf = wc.flops() / (ch_ms * 1e-3) / 1e12
+        chunked = {"workload": f"causal chunked prefill B={wc.B} Hq={wc.Hq} Hkv={wc.Hkv} Sq={wc.Sq} "
+                               f"Skv={wc.Skv} (query block after a {wc.Skv - wc.Sq}-token prefix) d={wc.d} bf16",
+                   "kv_splits": n_sp, "kernels": "prefill_bf16_kernel<128,causal> (split-KV) + combine_lse",
+                   "ms": round(ch_ms, 4), "tflops": round(ch_tf, 2),
+                   "pct_mfma_peak": round(100 * ch_tf / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "algorithmic_tflop": round(wc.flops() / 1e12, 6),
+                   "traffic": measured_traffic("chunked"),
+                   "traffic_unit": "HBM bytes per call, split-KV prefill + merge (fetch + write)"}
+        del qc, kc2, vc2, oc, lsec
 
     pf_flops = wp.flops()
     pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12 if do_pf else 0.0
@@ -245,6 +283,8 @@ def main():
         },
         "device": torch.cuda.get_device_name(dev),
     }
+    if chunked is not None:
+        result["chunked_prefill"] = chunked
     if not args.no_cpu_baseline:
         del q, k, v, o, lse, qd, kc, vc, part_o, part_lse, od, lsed
         torch.cuda.empty_cache()
