@@ -47,7 +47,7 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "bf17bc2bf59fe0c8",
                 "fetch_kib": 146992, "write_kib": 133123},
-    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "81d7970cf0f2d9a1",
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "0d37c578dc2e19f6",
                "fetch_kib": 262478 + 4172, "write_kib": 8704 + 72},
     "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "8bab83e9653b1752",
                 "fetch_kib": 250896 + 16917, "write_kib": 33280 + 8448},

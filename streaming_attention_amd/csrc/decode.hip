@@ -12,13 +12,15 @@
 //   * One workgroup per (sequence, KV head, split), 4 waves.  The split's keys
 //     are taken 32 at a time; wave w handles chunks w, w + 4, ...  Each wave
 //     keeps its own running (m, l, O) and double-buffers its next chunk's K and
-//     V in registers, so every wave has 16 KB of loads in flight while it
-//     computes.  At the end the four wave states are merged through LDS with
-//     the same log-sum-exp rule as the split merge.
-//   * Scores are S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from global
-//     memory straight into the A operand, Q of the G <= 16 heads as the B
-//     operand, zero-padded to 16 columns).  Each lane owns one query column and
-//     8 of the chunk's 32 keys; the other keys of that query sit in lanes
+//     V in registers (non-temporal loads: every byte is read exactly once), so
+//     every wave has 16 KB of loads in flight while it computes.  At the end
+//     the four wave states are merged through LDS with the same log-sum-exp
+//     rule as the split merge.
+//   * Scores are S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows loaded
+//     coalesced, whole 256-byte rows per 16 lanes, staged through a per-wave
+//     LDS region and read back as the A operand; Q of the G <= 16 heads as the
+//     B operand, zero-padded to 16 columns).  Each lane owns one query column
+//     and 8 of the chunk's 32 keys; the other keys of that query sit in lanes
 //     l ^ 16, l ^ 32, l ^ 48.
 //   * O^T += V^T P^T: P^T is 8 accumulator registers of S^T rounded to bf16;
 //     V^T comes from a per-wave LDS region that V is written into transposed
