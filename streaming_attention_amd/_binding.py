@@ -110,20 +110,20 @@ def _check_prefill_args(q, k, v):
     return B, Hq, Hkv, Sq, Skv, d
 
 
-# Workgroups the prefill launch should reach to occupy the GPU: two per
-# compute unit of the MI355X (256 CUs), which is what the kernel's register
-# and LDS budget lets one CU hold.
-_PREFILL_WG_TARGET = 2 * 256
+# The bf16 prefill kernel runs 256 stacked query rows per workgroup and one
+# workgroup per compute unit (its register budget); the MI355X has 256 CUs.
+_PREFILL_ROWS_PER_WG = 256
+_PREFILL_WG_TARGET = 256
 
 
 def prefill_splits(B: int, Hq: int, Hkv: int, Sq: int, Skv: int, dtype=torch.bfloat16) -> int:
-    """KV splits for a prefill: 1 when the query blocks alone give enough
-    workgroups, else enough splits to reach the target, keeping at least 16
-    key tiles (1024 keys) per split.  A scheduling choice: any split count
+    """KV splits for a prefill: 1 when the query blocks alone fill the GPU
+    (one workgroup per CU), else enough splits to reach that, keeping at least
+    16 key tiles (1024 keys) per split.  A scheduling choice: any split count
     gives the same result up to rounding."""
     if dtype != torch.bfloat16:
         return 1
-    blocks = -(-(Hq // Hkv) * Sq // 128) * B * Hkv
+    blocks = -(-(Hq // Hkv) * Sq // _PREFILL_ROWS_PER_WG) * B * Hkv
     if blocks == 0 or blocks >= _PREFILL_WG_TARGET:
         return 1
     tiles = -(-Skv // 64)

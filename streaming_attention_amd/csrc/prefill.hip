@@ -159,20 +159,21 @@ using Parity = std::integral_constant<int, P>;
 // tc.split -- tiles [s T, min((s + 1) T, all tiles)) with T = ceil(tiles /
 // n_splits), intersected with the causal extent -- and writes the normalised
 // fp32 partial (O over those keys, their LSE) in place of O and LSE.
-template <int D, bool CAUSAL, int QB>
-__global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
+template <int D, bool CAUSAL, int QB, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
     float c, int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  constexpr int BM = 128 * QB;              // stacked query rows per workgroup
+  constexpr int NT = 64 * NW;               // threads per workgroup
+  constexpr int BM = 32 * QB * NW;          // stacked query rows per workgroup
   constexpr int RW = 32 * QB;               // rows per wave
   constexpr int RB = 2 * D;                 // bytes per K / V row
   constexpr int U = D / 8;                  // 16-byte units per row
   constexpr int TB = kBN * RB;              // bytes per tile
-  constexpr int NLD = kBN * U / kThreads;   // direct loads per thread per tile (4 or 2)
+  constexpr int NLD = kBN * U / NT;         // direct loads per thread per tile
   constexpr int DS = D / 16;                // MFMA k-steps over d for S^T
   constexpr int DB = D / 32;                // 32-row d blocks of O^T
-  static_assert(NLD * kThreads == kBN * U, "a tile is a whole number of wave loads");
+  static_assert(NLD * NT == kBN * U, "a tile is a whole number of wave loads");
   auto sk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
   auto sv = [](int r) { return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); };
 
@@ -250,18 +251,18 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
   uint32_t k_src[NLD], v_src[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int p = 64 * (4 * j + w) + l;
+    const int p = 64 * (NW * j + w) + l;
     const int r = p / U, u = p % U;
     k_src[j] = (uint32_t)(r * RB + 16 * (u ^ sk(r)));
     v_src[j] = (uint32_t)(r * RB + 32 * ((u >> 1) ^ sv(r)) + 16 * (u & 1));
   }
   auto load_k = [&](int kt, lds_t* dst) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) load_to_lds16(rk, dst + 1024 * (4 * j + w), k_src[j], (uint32_t)kt * TB);
+    for (int j = 0; j < NLD; ++j) load_to_lds16(rk, dst + 1024 * (NW * j + w), k_src[j], (uint32_t)kt * TB);
   };
   auto load_v = [&](int kt, lds_t* dst) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) load_to_lds16(rv, dst + 1024 * (4 * j + w), v_src[j], (uint32_t)kt * TB);
+    for (int j = 0; j < NLD; ++j) load_to_lds16(rv, dst + 1024 * (NW * j + w), v_src[j], (uint32_t)kt * TB);
   };
 
   // Operand read offsets.  Score A operand (K): row 32 kb + lr, logical unit
@@ -482,8 +483,8 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void prefill_bf16_kernel(
     load_k(kt_lo + 1, kbuf[1]);
     // V slot 1 plays tile -1 in iteration 0: zero it, so 0 * V stays 0.
 #pragma unroll
-    for (int i = 0; i < TB / (16 * kThreads); ++i)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vbuf[1] + 16 * (tid + kThreads * i)) =
+    for (int i = 0; i < TB / (16 * NT); ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vbuf[1] + 16 * (tid + NT * i)) =
           u32x4{0u, 0u, 0u, 0u};
     wait_lds_loads();
     __syncthreads();
@@ -732,26 +733,30 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const dim3 blk(kThreads);
   if (a.bf16) {
     // One 32-row block per wave.  (Two blocks per wave halve the LDS bytes per
-    // MFMA but, at one wave per SIMD, measured slower on the 70B-shape prefill:
-    // 756 vs 941 TFLOP/s, the compiler shuttling accumulators between AGPRs
-    // and VGPRs.)
-    const dim3 g((unsigned)((rows + 127) / 128 * groups * a.n_splits));
-#define SA_LAUNCH_BF16(DD, CC, QQ)                                                                      \
-  hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, QQ>), g, blk, 0, stream, (const bf16*)a.q,          \
-                     (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,     \
-                     a.Skv, c, a.n_splits, a.part_o, a.part_lse)
+    // MFMA but spill at one wave per SIMD: the compiler shuttles the output
+    // accumulators between AGPRs and VGPRs.)  8 waves (256 rows) per
+    // workgroup, one workgroup per CU, whenever that still gives every CU a
+    // workgroup: each K/V tile brought into LDS then serves twice the rows.
+    // Smaller problems take 4-wave workgroups, two per CU.
+    const long long wg8 = (rows + 255) / 256 * groups * a.n_splits;
+    const bool eight = wg8 >= kNumCUs;
+    const long long nwg = eight ? wg8 : (rows + 127) / 128 * groups * a.n_splits;
+    const dim3 g((unsigned)nwg), blk_w(eight ? 512 : 256);
+#define SA_LAUNCH_BF16(DD, CC)                                                                           \
+  do {                                                                                                   \
+    if (eight)                                                                                           \
+      hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, 8>), g, blk_w, 0, stream, (const bf16*)a.q,   \
+                         (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,  \
+                         a.Skv, c, a.n_splits, a.part_o, a.part_lse);                                    \
+    else                                                                                                 \
+      hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, 4>), g, blk_w, 0, stream, (const bf16*)a.q,   \
+                         (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,  \
+                         a.Skv, c, a.n_splits, a.part_o, a.part_lse);                                    \
+  } while (0)
     if (a.d == 128) {
-      if (a.causal) {
-        SA_LAUNCH_BF16(128, true, 1);
-      } else {
-        SA_LAUNCH_BF16(128, false, 1);
-      }
+      if (a.causal) SA_LAUNCH_BF16(128, true); else SA_LAUNCH_BF16(128, false);
     } else {
-      if (a.causal) {
-        SA_LAUNCH_BF16(64, true, 1);
-      } else {
-        SA_LAUNCH_BF16(64, false, 1);
-      }
+      if (a.causal) SA_LAUNCH_BF16(64, true); else SA_LAUNCH_BF16(64, false);
     }
 #undef SA_LAUNCH_BF16
   } else {

@@ -151,10 +151,10 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
 
 
 def test_prefill_splits_heuristic():
-    assert sa.prefill_splits(1, 64, 8, 512, 66048) == 2        # 256 query blocks after a 64K prefix
-    assert sa.prefill_splits(1, 64, 8, 8192, 8192) == 1        # 4096 blocks already
+    assert sa.prefill_splits(1, 64, 8, 512, 66048) == 2        # 128 blocks of 256 rows after a 64K prefix
+    assert sa.prefill_splits(1, 64, 8, 8192, 8192) == 1        # 2048 blocks already
     assert sa.prefill_splits(1, 64, 8, 512, 66048, torch.float32) == 1
-    assert sa.prefill_splits(1, 8, 8, 64, 1 << 20) == 64       # few rows, long prefix: 8 blocks x 64
+    assert sa.prefill_splits(1, 8, 8, 64, 1 << 20) == 32       # few rows, long prefix: 8 blocks x 32
     assert sa.prefill_splits(1, 8, 1, 200, 333) == 1           # too few key tiles to split
 
 

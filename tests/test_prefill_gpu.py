@@ -296,3 +296,35 @@ def test_split_prefill_matches_unsplit_on_the_chunked_shape_rows():
         for o, l in ((o1, l1), (o2, l2)):
             assert_o(o[0, h, rows], O_ref, "bf16")
             assert_lse(l[0, h, rows], L_ref, "bf16")
+
+
+# Shapes large enough for the 8-wave (256-row) workgroups, d = 64 and 128,
+# causal and not, checked on sampled rows (the small shapes above run the
+# 4-wave launch).
+EIGHT_WAVE = [
+    # B, Hq, Hkv, Sq, Skv, d, causal
+    (1, 32, 32, 2048, 2048, 64, False),
+    (1, 64, 8, 1024, 1500, 128, False),
+    (2, 16, 2, 2048, 2048, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal", EIGHT_WAVE)
+def test_eight_wave_launch_sampled_rows(B, Hq, Hkv, Sq, Skv, d, causal):
+    assert -(-(Hq // Hkv) * Sq // 256) * B * Hkv >= 256      # the launch picks 8-wave workgroups
+    g = torch.Generator(device=DEV).manual_seed(3000 + Sq + Skv + d)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = sa.prefill(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 255, 256, Sq // 2, Sq - 1]
+    G = Hq // Hkv
+    for b in range(B):
+        for h in (0, Hq // 2 + 1, Hq - 1):
+            kvh = h // G
+            O_ref, L_ref = oracle.attention_rows(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, kvh:kvh + 1]),
+                                                 f64(v[b:b + 1, kvh:kvh + 1]), scale, causal, 0, 0, rows)
+            assert_o(o[b, h, rows], O_ref, "bf16", f"O b{b} h{h}")
+            assert_lse(lse[b, h, rows], L_ref, "bf16", f"LSE b{b} h{h}")
