@@ -29,5 +29,6 @@ from .attn_f64 import (  # noqa: F401
     attention_key_range,
     merge_partials,
     decode_attention,
+    paged_attention,
     visible_keys,
 )

@@ -66,7 +66,7 @@ def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float,
     """
     S = scale * (qh @ kh.T)                          # [n, Skv]
     S = np.where(vis, S, -np.inf)
-    m = S.max(axis=1)                                # -inf on empty rows
+    m = S.max(axis=1, initial=-np.inf)               # -inf on empty rows (and for Skv = 0)
     m_safe = np.where(np.isfinite(m), m, 0.0)
     E = np.where(vis, np.exp(S - m_safe[:, None]), 0.0)
     l = E.sum(axis=1)
@@ -278,6 +278,43 @@ def decode_attention(q, k_cache, v_cache, kv_len, scale: float):
         q = q[:, :, None, :]
     O, L = attention(q, k_cache, v_cache, scale, causal=False, kv_len=kv_len)
     return O[:, :, 0, :], L[:, :, 0]
+
+
+def paged_attention(q, k_pages, v_pages, block_table, kv_len, scale: float):
+    """Multi-token decode over a paged KV cache: every sequence's ``T_q`` query
+    tokens are the last ``T_q`` positions of its ``kv_len[b]`` valid keys and
+    attend causally (bottom-right) to them.
+
+    "ADR-0060" section 0.5.3: the query block carries its global start and
+    length (``q_block_meta {q_start, T_q}``, here ``q_start = kv_len[b] - T_q``),
+    and the kernel derives its valid length from a counter (section 2.2,
+    ``my_len``; here ``kv_len[b]``).  Section 2.1 lets the keys of a sequence sit
+    in a non-contiguous placement that plain arithmetic maps back to global
+    positions; here that map is a block table: logical page ``p`` of sequence
+    ``b`` (keys ``p*page .. p*page + page - 1``) is physical page
+    ``block_table[b, p]`` of the pool.
+
+    ``q [B, Hq, T_q, d]``; ``k_pages, v_pages [num_pages, Hkv, page, d]``;
+    ``block_table [B, max_pages]`` (entries past a sequence's last page are
+    ignored); ``kv_len [B]``.  The sequence's keys are gathered page by page
+    into a contiguous ``[Hkv, kv_len[b], d]`` cache and the definition
+    (``attention``, causal) is applied to it.  Returns ``O [B, Hq, T_q, d]`` and
+    ``LSE [B, Hq, T_q]`` (float64).
+    """
+    q, k_pages, v_pages = _f64(q), _f64(k_pages), _f64(v_pages)
+    block_table = np.asarray(block_table, dtype=np.int64)
+    B, Hq, T_q, d = q.shape
+    page = k_pages.shape[2]
+    O = np.zeros((B, Hq, T_q, v_pages.shape[3]))
+    L = np.zeros((B, Hq, T_q))
+    Hkv, dk, dv = k_pages.shape[1], k_pages.shape[3], v_pages.shape[3]
+    for b in range(B):
+        n = int(kv_len[b])
+        ids = block_table[b, :-(-n // page)]
+        kb = np.concatenate([np.zeros((Hkv, 0, dk))] + [k_pages[i] for i in ids], axis=1)[:, :n]
+        vb = np.concatenate([np.zeros((Hkv, 0, dv))] + [v_pages[i] for i in ids], axis=1)[:, :n]
+        O[b], L[b] = attention(q[b:b + 1], kb[None], vb[None], scale, True)
+    return O, L
 
 
 def lse_of_scores(scores) -> float:

@@ -389,6 +389,66 @@ def check_key_range_partials(seed=11):
         _close(L, full[1], 1e-12, f"key range merge LSE trial {trial}")
 
 
+def _pages_from_contiguous(k, page, order):
+    """Cut a contiguous cache [B, Hkv, S, d] into pages [B * n_pages, Hkv, page, d]
+    placed in the pool at positions given by ``order`` (a permutation); returns
+    the pool and the block table that undoes the placement.  Plain slicing."""
+    B, Hkv, S, d = k.shape
+    n_pages = -(-S // page)
+    padded = np.zeros((B, Hkv, n_pages * page, d))
+    padded[:, :, :S] = k
+    pool = np.zeros((B * n_pages, Hkv, page, d))
+    table = np.zeros((B, n_pages), dtype=np.int64)
+    for b in range(B):
+        for p_ in range(n_pages):
+            slot = int(order[b * n_pages + p_])
+            pool[slot] = padded[b, :, p_ * page:(p_ + 1) * page]
+            table[b, p_] = slot
+    return pool, table
+
+
+def check_paged_attention(seed=12):
+    """Multi-token decode over pages: scalar brute force on the gathered keys
+    (bottom-right causal within each sequence's valid length), the result does
+    not depend on where the pages sit in the pool or on table entries past a
+    sequence's last page, and T_q = 1 equals decode_attention."""
+    r = _rng(seed)
+    B, Hq, Hkv, T_q, S, d, page = 3, 4, 2, 3, 11, 3, 4
+    q = r.standard_normal((B, Hq, T_q, d))
+    k = r.standard_normal((B, Hkv, S, d))
+    v = r.standard_normal((B, Hkv, S, d))
+    lens = [11, 5, 2]                        # the last one is shorter than T_q
+    order = r.permutation(B * (-(-S // page)))
+    kp, table = _pages_from_contiguous(k, page, order)
+    vp, _ = _pages_from_contiguous(v, page, order)
+    O, L = oracle.paged_attention(q, kp, vp, table, lens, 0.8)
+    for b in range(B):
+        n = lens[b]
+        Ob, Lb = brute_force(q[b:b + 1].tolist(), k[b:b + 1, :, :n].tolist(), v[b:b + 1, :, :n].tolist(), 0.8, True)
+        _close(O[b], Ob[0], 1e-12, f"paged O seq {b}")
+        _close(L[b], Lb[0], 1e-12, f"paged LSE seq {b}")
+    # another placement of the same pages, and garbage past each sequence's pages
+    order2 = r.permutation(len(order))
+    kp2, table2 = _pages_from_contiguous(k, page, order2)
+    vp2, _ = _pages_from_contiguous(v, page, order2)
+    for b in range(B):
+        used = -(-lens[b] // page)
+        table2[b, used:] = r.integers(0, len(order), table2.shape[1] - used)
+    O2, L2 = oracle.paged_attention(q, kp2, vp2, table2, lens, 0.8)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2), "page placement changed the result"
+    # one query token: the decode definition
+    O1, L1 = oracle.paged_attention(q[:, :, -1:], kp, vp, table, lens, 0.8)
+    kc = np.zeros((B, Hkv, S, d))
+    vc = np.zeros((B, Hkv, S, d))
+    kc[:], vc[:] = k, v
+    Od, Ld = oracle.decode_attention(q[:, :, -1], kc, vc, lens, 0.8)
+    _close(O1[:, :, 0], Od, 1e-12, "paged T_q=1 O == decode")
+    _close(L1[:, :, 0], Ld, 1e-12, "paged T_q=1 LSE == decode")
+    # a sequence without keys
+    O0, L0 = oracle.paged_attention(q[:1], kp, vp, table[:1], [0], 0.8)
+    assert np.all(O0 == 0) and np.all(np.isneginf(L0))
+
+
 def check_empty_rows():
     """kv_len = 0 gives O = 0 and LSE = -inf."""
     q = np.ones((2, 2, 1, 3))
@@ -403,5 +463,6 @@ ALL_CHECKS = [
     check_brute_force, check_golden, check_golden_merge, check_zero_k, check_one_hot,
     check_ties, check_single_key, check_online_equals_two_pass, check_merge_any_partition,
     check_gqa_equals_repeated_mha, check_chunked_is_tail, check_scale_and_permutation,
-    check_partial_matches_restricted_definition, check_key_range_partials, check_empty_rows,
+    check_partial_matches_restricted_definition, check_key_range_partials, check_paged_attention,
+    check_empty_rows,
 ]

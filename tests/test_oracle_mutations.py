@@ -143,6 +143,25 @@ def _key_range_no_causal(q, k, v, scale, causal, key_lo, key_hi):
 ORIG_KEY_RANGE = oa.attention_key_range
 
 
+def _paged_logical_pages(q, k_pages, v_pages, block_table, kv_len, scale):
+    n = np.asarray(block_table).shape[1]
+    ident = np.tile(np.arange(n), (len(kv_len), 1))
+    return ORIG_PAGED(q, k_pages, v_pages, ident, kv_len, scale)          # mistake: table ignored
+
+
+def _paged_top_left(q, k_pages, v_pages, block_table, kv_len, scale):
+    O, L = ORIG_PAGED(q, k_pages, v_pages, block_table, kv_len, scale)
+    T_q = np.asarray(q).shape[2]
+    if T_q > 1:                                                            # mistake: queries at 0 .. T_q-1
+        big = [max(int(n), 1) for n in kv_len]
+        O2, L2 = ORIG_PAGED(q, k_pages, v_pages, block_table, [min(T_q, n) for n in big], scale)
+        return O2, L2
+    return O, L
+
+
+ORIG_PAGED = oa.paged_attention
+
+
 MUTATIONS = {
     "top_left_causal": ("visible_keys", _top_left_visible),
     "diagonal_hidden": ("visible_keys", _strict_diagonal),
@@ -155,6 +174,8 @@ MUTATIONS = {
     "partial_off_by_one": ("partial_attention", _partial_off_by_one),
     "key_range_inclusive_end": ("attention_key_range", _key_range_half_open_wrong),
     "key_range_no_causal": ("attention_key_range", _key_range_no_causal),
+    "paged_table_ignored": ("paged_attention", _paged_logical_pages),
+    "paged_top_left": ("paged_attention", _paged_top_left),
 }
 
 
