@@ -11,8 +11,9 @@ Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s
 (4 * d * visible (q, k) pairs per head / prefill kernel time); the decode
 throughput in KV GB/s (every valid K and V byte once / split + combine time)
 is reported next to it.  Outside the step, the chunked prefill (512 queries
-after a 65536-token prefix, split-KV + merge) is timed on its own and reported
-as `chunked_prefill`.  Kernel times come from HIP events recorded on the
+after a 65536-token prefix, split-KV + merge) and the multi-token decode over a
+paged cache (16 sequences x 4 tokens, lengths 1K-32K) are timed on their own
+and reported as `chunked_prefill` and `paged_decode`.  Kernel times come from HIP events recorded on the
 stream the kernels run on, over the timed steps.  The float64 oracle, timed on
 the host cores on a bounded sample of the same prefill workload, is reported as
 `cpu_baseline` (a baseline only).
@@ -73,10 +74,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "chunked", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "chunked", "paged", "copy"], default="all",
                     help="run only one part (for per-kernel profiling runs): one half of the step, the "
-                         "chunked prefill, or 'copy', a plain 1 GiB device copy that is the reference for "
-                         "scaling HBM byte counters")
+                         "chunked prefill, the paged multi-token decode, or 'copy', a plain 1 GiB device copy "
+                         "that is the reference for scaling HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -169,6 +170,7 @@ def main():
     do_pf = args.only in ("all", "prefill")
     do_dc = args.only in ("all", "decode")
     do_ch = args.only in ("all", "chunked")
+    do_pg = args.only in ("all", "paged")
 
     def step(i=None):
         if i is not None:
@@ -228,6 +230,34 @@ def main():
                    "traffic_unit": "HBM bytes per call, split-KV prefill + merge (fetch + write)"}
         del qc, kc2, vc2, oc, lsec
 
+    paged = None
+    if do_pg:   # multi-token decode over a paged cache, timed on its own (not part of the step)
+        wg = W.PAGED_DECODE
+        qg, kpg, vpg, tbl, lens_g = W.paged_inputs(wg, dev)
+        tbl_d, lens_d = tbl.to(dev), lens_g.to(dev)
+        og = torch.empty((wg.B, wg.Hq, wg.T_q, wg.d), dtype=torch.bfloat16, device=dev)
+        lseg = torch.empty((wg.B, wg.Hq, wg.T_q), dtype=torch.float32, device=dev)
+        n_sp = sa.paged_splits(wg.B, wg.Hq, wg.Hkv, wg.T_q, tbl.shape[1])
+        for _ in range(args.warmup):
+            sa.decode_paged(qg, kpg, vpg, tbl_d, lens_d, scale=wg.scale, out=og, lse=lseg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            sa.decode_paged(qg, kpg, vpg, tbl_d, lens_d, scale=wg.scale, out=og, lse=lseg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pg_ms = e0.elapsed_time(e1) / args.steps
+        pg_bytes = W.decode_kv_bytes(lens_g, wg.Hkv, wg.d)
+        pg_gbs = pg_bytes / (pg_ms * 1e-3) / 1e9
+        paged = {"workload": f"multi-token decode over a paged cache: B={wg.B} T_q={wg.T_q} Hq={wg.Hq} Hkv={wg.Hkv} "
+                             f"d={wg.d} bf16, lengths U[{wg.len_lo},{wg.len_hi}] (sum {int(lens_g.sum())}), "
+                             f"pages of {wg.page} shuffled in the pool",
+                 "kv_splits": n_sp, "kernels": "prefill_bf16_kernel<128,causal,paged> (split-KV) + combine_lse",
+                 "us": round(pg_ms * 1e3, 2), "kv_gbs": round(pg_gbs, 1),
+                 "pct_hbm_peak": round(100 * pg_gbs / HBM_PEAK_GBS, 2), "kv_bytes": pg_bytes}
+        del qg, kpg, vpg, tbl_d, lens_d, og, lseg
+
     pf_flops = wp.flops()
     pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12 if do_pf else 0.0
     kv_bytes = W.decode_kv_bytes(lens, wd.Hkv, wd.d)
@@ -285,6 +315,8 @@ def main():
     }
     if chunked is not None:
         result["chunked_prefill"] = chunked
+    if paged is not None:
+        result["paged_decode"] = paged
     if not args.no_cpu_baseline:
         del q, k, v, o, lse, qd, kc, vc, part_o, part_lse, od, lsed
         torch.cuda.empty_cache()

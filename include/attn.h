@@ -12,6 +12,8 @@
  *                        splits that each yield a partial result
  *   attn_combine_lse     merge of the split partials by log-sum-exp
  *   attn_decode          the split-KV decode and the merge in one launch
+ *   attn_decode_paged    T_q >= 1 new tokens per sequence over a paged KV cache
+ *                        with per-sequence lengths (optionally split)
  *
  * The method is the one of "ADR-0060: AHBM GQA Fused Attention kernel
  * (Llama3-70B)": per-tile online softmax (its section 3), log-sum-exp merge of
@@ -210,6 +212,53 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 int32_t max_splits, int32_t dtype, float scale,
                 float* part_o, float* part_lse, int32_t* counters,
                 void* o, float* lse, void* stream);
+
+/*
+ * attn_decode_paged -- multi-token decode over a paged KV cache: every
+ * sequence b has T_q new query tokens, which are the last T_q of its kv_len[b]
+ * positions and attend causally (bottom-right) to its keys.  T_q = 1 is the
+ * ordinary decode.
+ *
+ * Defined by ADR-0060 section 0.5.3 (the query block carries its start and
+ * length, q_block_meta {q_start, T_q}; here q_start = kv_len[b] - T_q), section
+ * 2.2 (the kernel derives the valid length and read range from a counter; here
+ * kv_len[b]) and section 2.1 (a sequence's keys may sit in a non-contiguous
+ * placement that plain arithmetic maps back to global positions; here a block
+ * table), with the per-tile sequence of section 3 and the split merge of
+ * section 4.
+ *
+ *   q           [B, Hq, T_q, d]              bf16
+ *   k_pages     [num_pages, Hkv, 64, d]      bf16, page pool (a page holds 64
+ *   v_pages     [num_pages, Hkv, 64, d]      bf16   consecutive positions of one
+ *                                                   sequence for every KV head)
+ *   block_table [B, max_pages] int32 device: logical page p of sequence b
+ *               (positions 64 p .. 64 p + 63) is pool page block_table[b, p].
+ *               Entries are clamped into [0, num_pages); only the first
+ *               ceil(kv_len[b] / 64) entries of a row are read.
+ *   kv_len      [B] int32 device; clamped to [0, 64 * max_pages].  Pool rows at
+ *               or past kv_len[b] in the sequence's last page are never used.
+ *   num_splits  1 .. 256.  1: o [B, Hq, T_q, d] bf16 and lse [B, Hq, T_q] fp32
+ *               (may be NULL) are written; part_o / part_lse may be NULL.
+ *               > 1: part_o [B, Hq, T_q, num_splits, d] and part_lse
+ *               [B, Hq, T_q, num_splits] fp32 are written (split s of sequence
+ *               b covers keys [64 s c, min(64 (s + 1) c, kv_len[b])) with
+ *               c = ceil(ceil(kv_len[b] / 64) / num_splits)); o / lse are not
+ *               touched and may be NULL.  Merge with attn_combine_lse(part_o,
+ *               part_lse, NULL, B * Hq * T_q, 1, num_splits, d, o, lse,
+ *               ATTN_DTYPE_BF16, stream).
+ *
+ * A query token before the sequence's first key (kv_len[b] < T_q) and an
+ * empty split give O = 0 and LSE = -inf.
+ * Sizes: B, T_q >= 0 (0 is an empty call); Hq, Hkv >= 1, Hq % Hkv == 0;
+ * num_pages, max_pages >= 1 with 64 * max_pages < 2^31; d 64 or 128.
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED (dtype other than
+ * bf16, d not 64/128), ATTN_ERR_ALIGN (q, the pools and the written outputs
+ * must be 16-byte aligned).
+ */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* kv_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t T_q, int32_t num_pages,
+                      int32_t max_pages, int32_t d, int32_t num_splits, int32_t dtype, float scale,
+                      float* part_o, float* part_lse, void* o, float* lse, void* stream);
 
 /*
  * attn_combine_lse -- merge split partials into the final decode output.

@@ -91,6 +91,43 @@ int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* par
   return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* kv_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t T_q, int32_t num_pages,
+                      int32_t max_pages, int32_t d, int32_t num_splits, int32_t dtype, float scale, float* part_o,
+                      float* part_lse, void* o, float* lse, void* stream) {
+  if (B < 0 || T_q < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_pages < 1 || max_pages < 1)
+    return ATTN_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > 256) return ATTN_ERR_SHAPE;
+  if (!good_scale(scale)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  const long long G = Hq / Hkv;
+  if ((long long)max_pages * 64 > 0x7fffffffLL || G * T_q * d * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  const long long n_mt = (G * T_q + 127) / 128;
+  if (n_mt * (long long)B * Hkv * num_splits > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (B == 0 || T_q == 0) return ATTN_OK;
+  if (q == nullptr || k_pages == nullptr || v_pages == nullptr || block_table == nullptr || kv_len == nullptr)
+    return ATTN_ERR_NULL;
+  if (num_splits > 1 ? (part_o == nullptr || part_lse == nullptr) : o == nullptr) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) ||
+      (num_splits > 1 ? (!aligned16(part_o) || !aligned16(part_lse)) : (!aligned16(o) || !aligned16(lse))))
+    return ATTN_ERR_ALIGN;
+
+  sa::PrefillArgs a;
+  a.q = q; a.k = k_pages; a.v = v_pages;
+  a.o = num_splits > 1 ? nullptr : o;
+  a.lse = num_splits > 1 ? nullptr : lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = T_q; a.Skv = 0; a.d = d;
+  a.bf16 = true;
+  a.causal = true;
+  a.scale = scale;
+  a.n_splits = num_splits;
+  a.part_o = num_splits > 1 ? part_o : nullptr;
+  a.part_lse = num_splits > 1 ? part_lse : nullptr;
+  a.block_table = block_table; a.kv_len = kv_len; a.max_pages = max_pages; a.num_pages = num_pages;
+  return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
                         const int32_t* num_splits, int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
                         int32_t max_splits, int32_t dtype, float scale, float* part_o, float* part_lse,

@@ -22,6 +22,12 @@ struct PrefillArgs {
   int n_splits = 1;
   float* part_o = nullptr;
   float* part_lse = nullptr;
+  // Paged multi-token decode when block_table is non-null: k / v are page
+  // pools [num_pages, Hkv, 64, d], block_table [B, max_pages], kv_len [B].
+  const int32_t* block_table = nullptr;
+  const int32_t* kv_len = nullptr;
+  int max_pages = 0;
+  int num_pages = 0;
 };
 
 struct DecodeArgs {

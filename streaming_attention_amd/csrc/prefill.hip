@@ -159,11 +159,20 @@ using Parity = std::integral_constant<int, P>;
 // tc.split -- tiles [s T, min((s + 1) T, all tiles)) with T = ceil(tiles /
 // n_splits), intersected with the causal extent -- and writes the normalised
 // fp32 partial (O over those keys, their LSE) in place of O and LSE.
-template <int D, bool CAUSAL, int QB, int NW>
+//
+// Paged mode (PAGED): multi-token decode over a paged cache.  k and v are page
+// pools [num_pages, Hkv, kBN, D]; key tile kt of sequence b is pool page
+// block_table[b * max_pages + kt] (clamped into the pool); the sequence holds
+// kv_len[b] keys (clamped to [0, kBN * max_pages]) and its Sq query tokens are
+// its last Sq positions, so q_start = kv_len[b] - Sq may be negative (rows
+// before the first key see nothing).  Skv is unused.  Each tile gets its own
+// buffer resource over the page's valid rows, so rows past kv_len read zero.
+template <int D, bool CAUSAL, int QB, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
-    float c, int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float c, int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len, int max_pages, int num_pages) {
   constexpr int NT = 64 * NW;               // threads per workgroup
   constexpr int BM = 32 * QB * NW;          // stacked query rows per workgroup
   constexpr int RW = 32 * QB;               // rows per wave
@@ -192,6 +201,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   const int n_groups = B * Hkv;
   const TileCoord tc = map_tile<BM>(blockIdx.x, n_groups * n_splits, n_splits, Hkv, n_mt, G, Sq);
   const int r0 = tc.mt * BM;
+  if constexpr (PAGED) {   // keys of this workgroup's sequence
+    const int len = kv_len[tc.b];
+    Skv = len < 0 ? 0 : (len > kBN * max_pages ? kBN * max_pages : len);
+  }
   const int q_start = Skv - Sq;
 
   const int tid = threadIdx.x;
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
 
   const size_t head0 = (size_t)tc.b * Hq + (size_t)tc.kvh * G;   // first query head of group
   const bf16* qg = q + head0 * Sq * D;
-  const size_t kvoff = ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
+  const size_t kvoff = PAGED ? 0 : ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
 
   // This lane's query rows (one per row block) and their global positions.
   int row[QB], pos[QB];
@@ -219,10 +232,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   int kt_lo = tc.split * tiles_per_split;
   int kt_hi = min(tiles_all, kt_lo + tiles_per_split);
   int wave_tmin = 0x3fffffff;
+  // A wave whose rows all lie past the group's last row (small query blocks,
+  // e.g. a few decode tokens) only helps load the tiles.
+  const bool wave_active = r0 + RW * w < rows_total;
   if (CAUSAL) {
     int tmin, tmax;
     row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, tmin, tmax);
-    kt_hi = min(kt_hi, (q_start + tmax) / kBN + 1);
+    const int vis_end = q_start + tmax + 1;   // keys seen by the block's last position
+    kt_hi = min(kt_hi, vis_end > 0 ? (vis_end + kBN - 1) / kBN : 0);
     const int wA = r0 + RW * w, wB = min(r0 + RW * w + RW - 1, rows_total - 1);
     if (wA <= wB) {
       int a, bb;
@@ -246,8 +263,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   // swizzles.  Rows at or past Skv read as zero (their scores are masked to
   // -inf, so P = 0, and the zero V rows add nothing).  The tile advances through
   // the wave-uniform offset, so the loop spends no VALU on load addresses.
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Skv * RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Skv * RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, PAGED ? 0u : (uint32_t)Skv * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, PAGED ? 0u : (uint32_t)Skv * RB);
+  // Paged mode: a resource over the valid rows of tile kt's page (none past
+  // the sequence's last key, so such loads read zero).
+  auto page_rsrc = [&](const bf16* pool, int kt) {
+    int rows_v = Skv - kt * kBN;
+    rows_v = rows_v < 0 ? 0 : (rows_v > kBN ? kBN : rows_v);
+    int pg = kt < max_pages ? block_table[(size_t)tc.b * max_pages + kt] : 0;
+    pg = pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg);
+    return make_rsrc(pool + ((size_t)pg * Hkv + tc.kvh) * kBN * D, (uint32_t)(rows_v * RB));
+  };
   uint32_t k_src[NLD], v_src[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
@@ -257,12 +283,24 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     v_src[j] = (uint32_t)(r * RB + 32 * ((u >> 1) ^ sv(r)) + 16 * (u & 1));
   }
   auto load_k = [&](int kt, lds_t* dst) {
+    if constexpr (PAGED) {
+      const __amdgpu_buffer_rsrc_t r = page_rsrc(k, kt);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) load_to_lds16(rk, dst + 1024 * (NW * j + w), k_src[j], (uint32_t)kt * TB);
+      for (int j = 0; j < NLD; ++j) load_to_lds16(r, dst + 1024 * (NW * j + w), k_src[j], 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) load_to_lds16(rk, dst + 1024 * (NW * j + w), k_src[j], (uint32_t)kt * TB);
+    }
   };
   auto load_v = [&](int kt, lds_t* dst) {
+    if constexpr (PAGED) {
+      const __amdgpu_buffer_rsrc_t r = page_rsrc(v, kt);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) load_to_lds16(rv, dst + 1024 * (NW * j + w), v_src[j], (uint32_t)kt * TB);
+      for (int j = 0; j < NLD; ++j) load_to_lds16(r, dst + 1024 * (NW * j + w), v_src[j], 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) load_to_lds16(rv, dst + 1024 * (NW * j + w), v_src[j], (uint32_t)kt * TB);
+    }
   };
 
   // Operand read offsets.  Score A operand (K): row 32 kb + lr, logical unit
@@ -392,7 +430,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     for (int s = 0; s < DS; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = as_bf16x8(buf_ld16(rk, (uint32_t)((kt * kBN + 32 * kb + lr) * RB + 32 * s + 16 * hf), 0));
+        bf16x8 a;
+        if constexpr (PAGED)
+          a = as_bf16x8(buf_ld16(page_rsrc(k, kt), (uint32_t)((32 * kb + lr) * RB + 32 * s + 16 * hf), 0));
+        else
+          a = as_bf16x8(buf_ld16(rk, (uint32_t)((kt * kBN + 32 * kb + lr) * RB + 32 * s + 16 * hf), 0));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], S[qb][kb], 0, 0, 0);
@@ -494,8 +536,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) sA[qb][kb][j] = 0.f;
+    if (wave_active) {
 #pragma unroll
-    for (int i = 0; i < 2 * DS; ++i) score_mfma(kbuf[0], sA, i);
+      for (int i = 0; i < 2 * DS; ++i) score_mfma(kbuf[0], sA, i);
+    }
     __syncthreads();   // K slot 0 is reloaded in iteration 0
   }
   auto iteration = [&](auto parity, int kt, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
@@ -503,7 +547,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     constexpr int P = decltype(parity)::value;
     load_k(kt + 2, kbuf[P]);    // past the range these fill idle slots (zeros past Skv)
     load_v(kt, vbuf[P]);
-    step(kt, Scur, Snext, pf_prev, pf_new, kbuf[1 - P], vbuf[1 - P]);
+    if (wave_active) step(kt, Scur, Snext, pf_prev, pf_new, kbuf[1 - P], vbuf[1 - P]);
     wait_lds_loads();
     __syncthreads();
   };
@@ -511,7 +555,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     iteration(Parity<0>{}, kt, sA, sB, pfB, pfA);
     if (kt + 1 < kt_hi) iteration(Parity<1>{}, kt + 1, sB, sA, pfA, pfB);
   }
-  if (kt_hi > kt_lo) {   // P V of the last tile: V slot and P registers by its parity
+  if (kt_hi > kt_lo && wave_active) {   // P V of the last tile: V slot and P registers by its parity
     if ((kt_hi - kt_lo) & 1) {
 #pragma unroll
       for (int i = 0; i < 4 * DB; ++i) pv_mfma(vbuf[0], pfA, i);
@@ -739,19 +783,21 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     // workgroup: each K/V tile brought into LDS then serves twice the rows.
     // Smaller problems take 4-wave workgroups, two per CU.
     const long long wg8 = (rows + 255) / 256 * groups * a.n_splits;
-    const bool eight = wg8 >= kNumCUs;
+    const bool eight = rows > 128 && wg8 >= kNumCUs;
+    const bool paged = a.block_table != nullptr;
     const long long nwg = eight ? wg8 : (rows + 127) / 128 * groups * a.n_splits;
     const dim3 g((unsigned)nwg), blk_w(eight ? 512 : 256);
+#define SA_LAUNCH_ONE(DD, CC, WW, PG)                                                                    \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, WW, PG>), g, blk_w, 0, stream, (const bf16*)a.q,     \
+                     (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, c, \
+                     a.n_splits, a.part_o, a.part_lse, a.block_table, a.kv_len, a.max_pages, a.num_pages)
 #define SA_LAUNCH_BF16(DD, CC)                                                                           \
   do {                                                                                                   \
-    if (eight)                                                                                           \
-      hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, 8>), g, blk_w, 0, stream, (const bf16*)a.q,   \
-                         (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,  \
-                         a.Skv, c, a.n_splits, a.part_o, a.part_lse);                                    \
-    else                                                                                                 \
-      hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, 4>), g, blk_w, 0, stream, (const bf16*)a.q,   \
-                         (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq,  \
-                         a.Skv, c, a.n_splits, a.part_o, a.part_lse);                                    \
+    if (paged) {                                                                                         \
+      if (eight) SA_LAUNCH_ONE(DD, CC, 8, true); else SA_LAUNCH_ONE(DD, CC, 4, true);                   \
+    } else {                                                                                             \
+      if (eight) SA_LAUNCH_ONE(DD, CC, 8, false); else SA_LAUNCH_ONE(DD, CC, 4, false);                 \
+    }                                                                                                    \
   } while (0)
     if (a.d == 128) {
       if (a.causal) SA_LAUNCH_BF16(128, true); else SA_LAUNCH_BF16(128, false);
@@ -759,6 +805,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
       if (a.causal) SA_LAUNCH_BF16(64, true); else SA_LAUNCH_BF16(64, false);
     }
 #undef SA_LAUNCH_BF16
+#undef SA_LAUNCH_ONE
   } else {
     const dim3 g((unsigned)((rows + kBM - 1) / kBM * groups));
 #define SA_LAUNCH_F32(DD, CC)                                                                         \

@@ -83,7 +83,33 @@ class Decode:
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
 
 
-# The five workloads, smallest first.
+@dataclasses.dataclass(frozen=True)
+class PagedDecode:
+    """T_q new tokens per sequence over a paged KV cache (pages of 64
+    positions, shuffled in the pool), ragged lengths uniform in [len_lo, len_hi]."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    T_q: int
+    d: int
+    seed: int
+    len_lo: int
+    len_hi: int
+    spare_pages: int = 8          # pool pages no sequence uses (NaN-filled)
+    page: int = 64
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+# The workloads, smallest first.
 SINGLE_HEAD_F32 = Prefill("single_head_f32_s128_d64", B=1, Hq=1, Hkv=1, Sq=128, Skv=128,
                           d=64, dtype="f32", causal=False, seed=1)
 MHA_CAUSAL = Prefill("mha_causal_b2_h16_s1024_d64", B=2, Hq=16, Hkv=16, Sq=1024, Skv=1024,
@@ -97,6 +123,9 @@ RAGGED_DECODE = Decode("ragged_decode_b16_len1k_128k", B=16, Hq=64, Hkv=8, S_cap
                        splits=None, nan_padding=True)
 CHUNKED_PREFILL = Prefill("chunked_prefill_q512_prefix65536", B=1, Hq=64, Hkv=8, Sq=512,
                           Skv=65536 + 512, d=128, dtype="bf16", causal=True, seed=6)
+
+PAGED_DECODE = PagedDecode("paged_decode_b16_tq4_len1k_32k", B=16, Hq=64, Hkv=8, T_q=4, d=128, seed=7,
+                           len_lo=1024, len_hi=32768)
 
 PREFILL_WORKLOADS = [SINGLE_HEAD_F32, MHA_CAUSAL, GQA70B_PREFILL, CHUNKED_PREFILL]
 DECODE_WORKLOADS = [GQA70B_DECODE, RAGGED_DECODE]
@@ -155,3 +184,50 @@ def decode_inputs(w: Decode, device="cpu", *, B=None, S_cap=None, lengths=None):
 def decode_kv_bytes(lens, Hkv: int, d: int, elem_bytes: int = 2) -> int:
     """Algorithmic KV bytes of one decode step: every valid K and V byte once."""
     return int(sum(int(x) for x in lens)) * Hkv * d * elem_bytes * 2
+
+
+def paged_lengths(w: PagedDecode, B=None) -> torch.Tensor:
+    """Per-sequence KV lengths (int32, CPU), drawn first from the seed."""
+    B = w.B if B is None else B
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    return torch.randint(w.len_lo, w.len_hi + 1, (B,), generator=g).to(torch.int32)
+
+
+def paged_inputs(w: PagedDecode, device="cpu", *, B=None, lengths=None):
+    """Q ``[B,Hq,T_q,d]``, page pools ``[num_pages,Hkv,page,d]`` for K and V,
+    block table ``[B,max_pages]`` int32 and lengths ``[B]`` int32 (CPU).
+
+    Lengths come first (CPU generator), then the pool placement: a random
+    permutation of all pool pages (same CPU generator), consumed in sequence
+    order.  Then Q and each sequence's K and V (device generator), written page
+    by page to their pool slots.  Positions past a sequence's length in its
+    last page, and the spare pages, are NaN; unused block-table entries point
+    at a spare page.
+    """
+    B = w.B if B is None else B
+    gc = torch.Generator(device="cpu").manual_seed(w.seed)
+    drawn = torch.randint(w.len_lo, w.len_hi + 1, (B,), generator=gc).to(torch.int32)   # = paged_lengths
+    lens = drawn if lengths is None else lengths.to(torch.int32).cpu()
+    n_pages = [-(-int(n) // w.page) for n in lens]
+    max_pages = max(max(n_pages), 1)
+    total = sum(n_pages) + w.spare_pages
+    order = torch.randperm(total, generator=gc)
+    table = torch.full((B, max_pages), int(order[total - 1]), dtype=torch.int32)
+    g = torch.Generator(device=device).manual_seed(w.seed)
+    q = _randn((B, w.Hq, w.T_q, w.d), g, device, w.torch_dtype)
+    kp = torch.full((total, w.Hkv, w.page, w.d), float("nan"), dtype=w.torch_dtype, device=device)
+    vp = torch.full_like(kp, float("nan"))
+    nxt = 0
+    for b in range(B):
+        n = int(lens[b])
+        kb = _randn((w.Hkv, n_pages[b] * w.page, w.d), g, device, w.torch_dtype)
+        vb = _randn((w.Hkv, n_pages[b] * w.page, w.d), g, device, w.torch_dtype)
+        kb[:, n:] = float("nan")
+        vb[:, n:] = float("nan")
+        for p_ in range(n_pages[b]):
+            slot = int(order[nxt])
+            nxt += 1
+            table[b, p_] = slot
+            kp[slot] = kb[:, p_ * w.page:(p_ + 1) * w.page]
+            vp[slot] = vb[:, p_ * w.page:(p_ + 1) * w.page]
+    return q, kp, vp, table, lens

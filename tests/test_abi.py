@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
     for n in ("attn_prefill", "attn_prefill_splitkv", "attn_decode_splitkv", "attn_combine_lse", "attn_decode",
-              "attn_status_string"):
+              "attn_decode_paged", "attn_status_string"):
         assert n in names
 
 
@@ -69,6 +69,25 @@ def prefill_split(q=P, k=P, v=P, po=P, pl=P, B=1, Hq=8, Hkv=2, Sq=16, Skv=32, d=
 ])
 def test_prefill_splitkv_host_validation(kw, expect):
     assert prefill_split(**kw) == expect
+
+
+def paged(q=P, kp=P, vp=P, bt=P, kl=P, B=2, Hq=8, Hkv=2, T_q=4, num_pages=10, max_pages=4, d=128, n=1,
+          dtype=BF16, scale=0.088, po=P, pl=P, o=P, lse=P, stream=None):
+    return sa.lib().attn_decode_paged(q, kp, vp, bt, kl, B, Hq, Hkv, T_q, num_pages, max_pages, d, n, dtype, scale,
+                                      po, pl, o, lse, stream)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), NULL), (dict(kp=None), NULL), (dict(bt=None), NULL), (dict(kl=None), NULL),
+    (dict(o=None), NULL), (dict(n=2, po=None), NULL), (dict(n=2, o=None, lse=None, pl=None), NULL),
+    (dict(n=0), SHAPE), (dict(n=300), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(num_pages=0), SHAPE),
+    (dict(max_pages=0), SHAPE), (dict(T_q=-1), SHAPE), (dict(scale=0.0), SHAPE),
+    (dict(dtype=F32), UNSUP), (dict(d=80), UNSUP), (dict(max_pages=1 << 26), UNSUP),
+    (dict(q=MIS), ALIGN), (dict(kp=MIS), ALIGN), (dict(o=MIS), ALIGN), (dict(n=3, pl=MIS), ALIGN),
+    (dict(B=0), OK), (dict(T_q=0), OK), (dict(B=0, q=None, kp=None, bt=None), OK),
+])
+def test_decode_paged_host_validation(kw, expect):
+    assert paged(**kw) == expect
 
 
 def decode(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=100, d=128, max_splits=8,
@@ -156,6 +175,12 @@ def test_prefill_splits_heuristic():
     assert sa.prefill_splits(1, 64, 8, 512, 66048, torch.float32) == 1
     assert sa.prefill_splits(1, 8, 8, 64, 1 << 20) == 32       # few rows, long prefix: 8 blocks x 32
     assert sa.prefill_splits(1, 8, 1, 200, 333) == 1           # too few key tiles to split
+
+
+def test_paged_splits_heuristic():
+    assert sa.paged_splits(16, 64, 8, 4, 512) == 4      # 128 query blocks -> 4 splits
+    assert sa.paged_splits(1, 64, 8, 1, 512) == 64      # one sequence: split its keys widely
+    assert sa.paged_splits(64, 64, 8, 4, 8) == 1        # short sequences: no split
 
 
 def test_splits_for_lengths():

@@ -1,0 +1,106 @@
+"""attn_decode_paged on the GPU against the float64 oracle: several query
+tokens per sequence over a paged, shuffled KV cache with ragged lengths."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_attention_amd as sa
+from streaming_attention_amd import workloads as W
+from parity import assert_lse, assert_o, assert_rel_fro, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle_for(q, kp, vp, table, lens, scale, seqs):
+    """Oracle result of the listed sequences: their pages (only) copied to the
+    CPU as a small pool, the table remapped to it."""
+    out = {}
+    for b in seqs:
+        n = int(lens[b])
+        used = -(-n // W.PAGED_DECODE.page)
+        ids = table[b, :used].long().cpu()
+        kpool = f64(kp[ids.to(kp.device)]) if used else np.zeros((1,) + tuple(kp.shape[1:]))
+        vpool = f64(vp[ids.to(vp.device)]) if used else np.zeros((1,) + tuple(vp.shape[1:]))
+        t = np.arange(max(used, 1))[None, :]
+        out[b] = oracle.paged_attention(f64(q[b:b + 1]), kpool, vpool, t, [n], scale)
+    return out
+
+
+def _check(o, lse, q, kp, vp, table, lens, scale, seqs):
+    ref = _oracle_for(q, kp, vp, table, lens, scale, seqs)
+    for b in seqs:
+        O_ref, L_ref = ref[b]
+        assert_o(o[b:b + 1], O_ref, "bf16", f"O seq {b} len {int(lens[b])}")
+        assert_lse(lse[b:b + 1], L_ref, "bf16", f"LSE seq {b} len {int(lens[b])}")
+        if int(lens[b]) >= q.shape[2]:
+            assert_rel_fro(o[b:b + 1], O_ref, f"O seq {b}")
+
+
+# B, Hq, Hkv, T_q, lengths, d, splits (None = the binding's choice)
+SMALL = [
+    (3, 8, 2, 4, [141, 64, 3], 128, None),
+    (3, 8, 2, 4, [141, 64, 3], 128, 3),
+    (2, 16, 2, 1, [500, 1], 64, 2),          # one token: the ordinary decode
+    (2, 8, 8, 7, [300, 5], 128, 1),          # a sequence shorter than its query block
+    (1, 64, 8, 16, [2000], 128, 4),          # 128 stacked rows: one full row block
+    (1, 64, 8, 20, [700], 128, None),        # 160 rows: two row blocks
+    (2, 4, 1, 3, [0, 129], 64, 2),           # an empty sequence
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T_q,lens,d,splits", SMALL)
+def test_paged_decode_small(B, Hq, Hkv, T_q, lens, d, splits):
+    w = dataclasses.replace(W.PAGED_DECODE, B=B, Hq=Hq, Hkv=Hkv, T_q=T_q, d=d, seed=100 + sum(lens) + T_q)
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=torch.tensor(lens))
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=splits, scale=w.scale)
+    torch.cuda.synchronize()
+    _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(B))
+
+
+def test_paged_decode_matches_contiguous_decode_for_one_token():
+    """T_q = 1 over pages == attn_decode_splitkv + merge over the same keys laid
+    out contiguously."""
+    w = dataclasses.replace(W.PAGED_DECODE, B=3, T_q=1, seed=77)
+    lens = torch.tensor([1000, 64, 4097])
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=lens)
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), scale=w.scale)
+    S_cap = int(lens.max())
+    kc = torch.zeros((3, w.Hkv, S_cap, w.d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    for b in range(3):
+        n = int(lens[b])
+        pages = table[b, :-(-n // 64)].long().to(DEV)
+        kc[b, :, :n] = kp[pages].permute(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)[:, :n]
+        vc[b, :, :n] = vp[pages].permute(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)[:, :n]
+    o2, lse2 = sa.decode(q, kc, vc, lens_t.to(DEV), None, max_splits=8, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_o(o, o2.float(), "bf16")
+    assert_lse(lse, lse2.reshape(lse.shape), "bf16")
+
+
+def test_paged_decode_full_size_sampled_sequences():
+    """The measured workload (16 sequences, 4 tokens each, lengths 1K-32K,
+    shuffled pages, NaN past every length and in spare pages), in the
+    benchmark's launch shape: every output finite, sampled sequences exact."""
+    w = W.PAGED_DECODE
+    q, kp, vp, table, lens = W.paged_inputs(w, DEV)
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    shortest, longest = int(torch.argmin(lens)), int(torch.argmax(lens))
+    _check(o, lse, q, kp, vp, table, lens, w.scale, sorted({0, shortest, longest}))
+
+
+def test_paged_decode_repeat_is_bitwise():
+    w = dataclasses.replace(W.PAGED_DECODE, B=4, seed=91)
+    lens = torch.tensor([3000, 17, 640, 2048])
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=lens)
+    a = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=3)
+    b = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
