@@ -253,7 +253,8 @@ def main():
         paged = {"workload": f"multi-token decode over a paged cache: B={wg.B} T_q={wg.T_q} Hq={wg.Hq} Hkv={wg.Hkv} "
                              f"d={wg.d} bf16, lengths U[{wg.len_lo},{wg.len_hi}] (sum {int(lens_g.sum())}), "
                              f"pages of {wg.page} shuffled in the pool",
-                 "kv_splits": n_sp, "kernels": "prefill_bf16_kernel<128,causal,paged> (split-KV) + combine_lse",
+                 "kv_splits": n_sp,
+                 "kernels": "prefill_bf16_kernel<128,causal,paged> (split-KV) + combine_lse",
                  "us": round(pg_ms * 1e3, 2), "kv_gbs": round(pg_gbs, 1),
                  "pct_hbm_peak": round(100 * pg_gbs / HBM_PEAK_GBS, 2), "kv_bytes": pg_bytes}
         del qg, kpg, vpg, tbl_d, lens_d, og, lseg

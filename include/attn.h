@@ -240,12 +240,16 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
  *   num_splits  1 .. 256.  1: o [B, Hq, T_q, d] bf16 and lse [B, Hq, T_q] fp32
  *               (may be NULL) are written; part_o / part_lse may be NULL.
  *               > 1: part_o [B, Hq, T_q, num_splits, d] and part_lse
- *               [B, Hq, T_q, num_splits] fp32 are written (split s of sequence
- *               b covers keys [64 s c, min(64 (s + 1) c, kv_len[b])) with
- *               c = ceil(ceil(kv_len[b] / 64) / num_splits)); o / lse are not
- *               touched and may be NULL.  Merge with attn_combine_lse(part_o,
- *               part_lse, NULL, B * Hq * T_q, 1, num_splits, d, o, lse,
- *               ATTN_DTYPE_BF16, stream).
+ *               [B, Hq, T_q, num_splits] fp32 are written; o / lse are not
+ *               touched and may be NULL.
+ *   num_splits_seq  [B] int32 device, or NULL (num_splits for every sequence):
+ *               sequence b uses n_b = num_splits_seq[b] splits, clamped to
+ *               [1, num_splits]; ignored when num_splits is 1.  Split s < n_b
+ *               covers keys [64 s c, min(64 (s + 1) c, kv_len[b])) with
+ *               c = ceil(ceil(kv_len[b] / 64) / n_b); entries s >= n_b are not
+ *               written.  Merge with attn_combine_lse(part_o, part_lse,
+ *               num_splits_seq, B, Hq * T_q, num_splits, d, o, lse,
+ *               ATTN_DTYPE_BF16, stream): its rows are (b, head, token).
  *
  * A query token before the sequence's first key (kv_len[b] < T_q) and an
  * empty split give O = 0 and LSE = -inf.
@@ -256,9 +260,10 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
  * must be 16-byte aligned).
  */
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
-                      const int32_t* kv_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t T_q, int32_t num_pages,
-                      int32_t max_pages, int32_t d, int32_t num_splits, int32_t dtype, float scale,
-                      float* part_o, float* part_lse, void* o, float* lse, void* stream);
+                      const int32_t* kv_len, const int32_t* num_splits_seq, int32_t B, int32_t Hq, int32_t Hkv,
+                      int32_t T_q, int32_t num_pages, int32_t max_pages, int32_t d, int32_t num_splits,
+                      int32_t dtype, float scale, float* part_o, float* part_lse, void* o, float* lse,
+                      void* stream);
 
 /*
  * attn_combine_lse -- merge split partials into the final decode output.

@@ -92,9 +92,10 @@ int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* par
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
-                      const int32_t* kv_len, int32_t B, int32_t Hq, int32_t Hkv, int32_t T_q, int32_t num_pages,
-                      int32_t max_pages, int32_t d, int32_t num_splits, int32_t dtype, float scale, float* part_o,
-                      float* part_lse, void* o, float* lse, void* stream) {
+                      const int32_t* kv_len, const int32_t* num_splits_seq, int32_t B, int32_t Hq, int32_t Hkv,
+                      int32_t T_q, int32_t num_pages, int32_t max_pages, int32_t d, int32_t num_splits,
+                      int32_t dtype, float scale, float* part_o, float* part_lse, void* o, float* lse,
+                      void* stream) {
   if (B < 0 || T_q < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_pages < 1 || max_pages < 1)
     return ATTN_ERR_SHAPE;
   if (num_splits < 1 || num_splits > 256) return ATTN_ERR_SHAPE;
@@ -125,6 +126,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
   a.part_o = num_splits > 1 ? part_o : nullptr;
   a.part_lse = num_splits > 1 ? part_lse : nullptr;
   a.block_table = block_table; a.kv_len = kv_len; a.max_pages = max_pages; a.num_pages = num_pages;
+  a.seq_splits = num_splits > 1 ? num_splits_seq : nullptr;
   return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

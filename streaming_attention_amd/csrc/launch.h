@@ -28,6 +28,7 @@ struct PrefillArgs {
   const int32_t* kv_len = nullptr;
   int max_pages = 0;
   int num_pages = 0;
+  const int32_t* seq_splits = nullptr;   // per-sequence split counts (paged), or null
 };
 
 struct DecodeArgs {

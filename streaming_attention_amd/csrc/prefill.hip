@@ -167,12 +167,16 @@ using Parity = std::integral_constant<int, P>;
 // its last Sq positions, so q_start = kv_len[b] - Sq may be negative (rows
 // before the first key see nothing).  Skv is unused.  Each tile gets its own
 // buffer resource over the page's valid rows, so rows past kv_len read zero.
+// seq_splits (paged mode, may be null): sequence b uses only its first
+// seq_splits[b] (clamped to [1, n_splits]) splits, with the tile plan of that
+// count; workgroups of its other splits exit at once.
 template <int D, bool CAUSAL, int QB, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
     float c, int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len, int max_pages, int num_pages) {
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len, int max_pages, int num_pages,
+    const int32_t* __restrict__ seq_splits) {
   constexpr int NT = 64 * NW;               // threads per workgroup
   constexpr int BM = 32 * QB * NW;          // stacked query rows per workgroup
   constexpr int RW = 32 * QB;               // rows per wave
@@ -227,8 +231,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
 
   // Tile range of this workgroup (its KV split, cut at the causal extent) and
   // the mask-free bound per wave.
+  int n_sp = n_splits;
+  if (PAGED && seq_splits != nullptr) {
+    n_sp = seq_splits[tc.b];
+    n_sp = n_sp < 1 ? 1 : (n_sp > n_splits ? n_splits : n_sp);
+    if (tc.split >= n_sp) return;   // uniform over the workgroup: before any barrier
+  }
   const int tiles_all = (Skv + kBN - 1) / kBN;
-  const int tiles_per_split = (tiles_all + n_splits - 1) / n_splits;
+  const int tiles_per_split = (tiles_all + n_sp - 1) / n_sp;
   int kt_lo = tc.split * tiles_per_split;
   int kt_hi = min(tiles_all, kt_lo + tiles_per_split);
   int wave_tmin = 0x3fffffff;
@@ -790,7 +800,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
 #define SA_LAUNCH_ONE(DD, CC, WW, PG)                                                                    \
   hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, WW, PG>), g, blk_w, 0, stream, (const bf16*)a.q,     \
                      (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, c, \
-                     a.n_splits, a.part_o, a.part_lse, a.block_table, a.kv_len, a.max_pages, a.num_pages)
+                     a.n_splits, a.part_o, a.part_lse, a.block_table, a.kv_len, a.max_pages, a.num_pages, \
+                     a.seq_splits)
 #define SA_LAUNCH_BF16(DD, CC)                                                                           \
   do {                                                                                                   \
     if (paged) {                                                                                         \

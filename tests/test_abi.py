@@ -71,10 +71,10 @@ def test_prefill_splitkv_host_validation(kw, expect):
     assert prefill_split(**kw) == expect
 
 
-def paged(q=P, kp=P, vp=P, bt=P, kl=P, B=2, Hq=8, Hkv=2, T_q=4, num_pages=10, max_pages=4, d=128, n=1,
-          dtype=BF16, scale=0.088, po=P, pl=P, o=P, lse=P, stream=None):
-    return sa.lib().attn_decode_paged(q, kp, vp, bt, kl, B, Hq, Hkv, T_q, num_pages, max_pages, d, n, dtype, scale,
-                                      po, pl, o, lse, stream)
+def paged(q=P, kp=P, vp=P, bt=P, kl=P, ns=None, B=2, Hq=8, Hkv=2, T_q=4, num_pages=10, max_pages=4, d=128,
+          n=1, dtype=BF16, scale=0.088, po=P, pl=P, o=P, lse=P, stream=None):
+    return sa.lib().attn_decode_paged(q, kp, vp, bt, kl, ns, B, Hq, Hkv, T_q, num_pages, max_pages, d, n, dtype,
+                                      scale, po, pl, o, lse, stream)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -178,9 +178,9 @@ def test_prefill_splits_heuristic():
 
 
 def test_paged_splits_heuristic():
-    assert sa.paged_splits(16, 64, 8, 4, 512) == 4      # 128 query blocks -> 4 splits
-    assert sa.paged_splits(1, 64, 8, 1, 512) == 64      # one sequence: split its keys widely
-    assert sa.paged_splits(64, 64, 8, 4, 8) == 1        # short sequences: no split
+    assert sa.paged_splits(16, 64, 8, 4, 512) == 8      # 128 query blocks -> 8 splits
+    assert sa.paged_splits(1, 64, 8, 1, 4096) == 128    # one sequence: split its keys widely
+    assert sa.paged_splits(64, 64, 8, 4, 8) == 1        # 512 keys at most: no split
 
 
 def test_splits_for_lengths():

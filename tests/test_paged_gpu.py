@@ -104,3 +104,15 @@ def test_paged_decode_repeat_is_bitwise():
     b = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=3)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("kps", [64, 128, 200])
+def test_paged_decode_per_sequence_splits(kps):
+    """Split counts that differ per sequence (ceil(len / kps), partly clamped):
+    the merge reads each sequence's own count."""
+    w = dataclasses.replace(W.PAGED_DECODE, B=4, Hq=16, Hkv=2, T_q=3, seed=300 + kps)
+    lens = torch.tensor([1000, 1, 130, 700])
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=lens)
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), scale=w.scale, keys_per_split=kps)
+    torch.cuda.synchronize()
+    _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(4))
