@@ -46,12 +46,12 @@ METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQ
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "bf17bc2bf59fe0c8",
-                "fetch_kib": 146992, "write_kib": 133123},
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "17a11adc1ce6e20e",
+                "fetch_kib": 138465, "write_kib": 133120},
     "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "0d37c578dc2e19f6",
                "fetch_kib": 262478 + 4172, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "8bab83e9653b1752",
-                "fetch_kib": 250896 + 16917, "write_kib": 33280 + 8448},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "8181934023498632",
+                "fetch_kib": 140882 + 16917, "write_kib": 33280 + 8448},
 }
 
 
