@@ -245,6 +245,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   // A wave whose rows all lie past the group's last row (small query blocks,
   // e.g. a few decode tokens) only helps load the tiles.
   const bool wave_active = r0 + RW * w < rows_total;
+  // Causal: the workgroup sweeps to the last tile its latest row sees, but a
+  // wave with earlier rows needs only tiles [kt_lo, wave_end): from step
+  // wave_end + 1 on it only helps load tiles (step wave_end still runs: it
+  // adds the P V product of tile wave_end - 1).
+  int wave_end = 0x3fffffff;
   if (CAUSAL) {
     int tmin, tmax;
     row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, tmin, tmax);
@@ -255,6 +260,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
       int a, bb;
       row_range_positions(wA, wB, Sq, a, bb);
       wave_tmin = a;
+      const int wv_end = q_start + bb + 1;
+      wave_end = wv_end > 0 ? (wv_end + kBN - 1) / kBN : 0;
     }
   }
 
@@ -522,6 +529,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   kt_lo = __builtin_amdgcn_readfirstlane(kt_lo);
   kt_hi = __builtin_amdgcn_readfirstlane(kt_hi);
   wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
+  wave_end = __builtin_amdgcn_readfirstlane(min(wave_end, kt_hi));
   f32x16 sA[QB][2], sB[QB][2];
   bf16x8 pfA[QB][2][2], pfB[QB][2][2];
 #pragma unroll
@@ -557,7 +565,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     constexpr int P = decltype(parity)::value;
     load_k(kt + 2, kbuf[P]);    // past the range these fill idle slots (zeros past Skv)
     load_v(kt, vbuf[P]);
-    if (wave_active) step(kt, Scur, Snext, pf_prev, pf_new, kbuf[1 - P], vbuf[1 - P]);
+    if (wave_active && kt <= wave_end) step(kt, Scur, Snext, pf_prev, pf_new, kbuf[1 - P], vbuf[1 - P]);
     wait_lds_loads();
     __syncthreads();
   };
@@ -565,7 +573,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     iteration(Parity<0>{}, kt, sA, sB, pfB, pfA);
     if (kt + 1 < kt_hi) iteration(Parity<1>{}, kt + 1, sB, sA, pfA, pfB);
   }
-  if (kt_hi > kt_lo && wave_active) {   // P V of the last tile: V slot and P registers by its parity
+  // P V of the last tile (V slot and P registers by its parity), unless this
+  // wave stopped early: then that tile is wholly masked for it and step
+  // wave_end has already added its last real tile.
+  if (kt_hi > kt_lo && wave_active && wave_end >= kt_hi) {
     if ((kt_hi - kt_lo) & 1) {
 #pragma unroll
       for (int i = 0; i < 4 * DB; ++i) pv_mfma(vbuf[0], pfA, i);

@@ -328,3 +328,17 @@ def test_eight_wave_launch_sampled_rows(B, Hq, Hkv, Sq, Skv, d, causal):
                                                  f64(v[b:b + 1, kvh:kvh + 1]), scale, causal, 0, 0, rows)
             assert_o(o[b, h, rows], O_ref, "bf16", f"O b{b} h{h}")
             assert_lse(lse[b, h, rows], L_ref, "bf16", f"LSE b{b} h{h}")
+
+
+def test_lse_output_is_optional():
+    """lse = NULL writes O only, bitwise the same O as with the LSE output (both
+    launch shapes: 4-wave small, 8-wave large)."""
+    for (Hq, Hkv, S) in ((8, 2, 300), (64, 8, 2048)):
+        g = torch.Generator(device=DEV).manual_seed(4000 + S)
+        q = torch.randn((1, Hq, S, 128), generator=g, device=DEV).to(torch.bfloat16)
+        k = torch.randn((1, Hkv, S, 128), generator=g, device=DEV).to(torch.bfloat16)
+        v = torch.randn((1, Hkv, S, 128), generator=g, device=DEV).to(torch.bfloat16)
+        o1, _ = sa.prefill(q, k, v, causal=True)
+        o2 = sa.prefill(q, k, v, causal=True, return_lse=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
