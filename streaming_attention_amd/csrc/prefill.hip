@@ -127,9 +127,10 @@ __device__ __forceinline__ void row_range_positions(int rA, int rB, int Sq, int&
 // d values of 4 key rows, every lane receives one d column over 4 keys: the
 // transposed V operand, read straight from the row-major tile.
 //
-// QB = 32-row query blocks per wave (workgroup = 4 waves = 128 * QB stacked
-// rows).  QB = 2 halves the LDS bytes per MFMA (every K and V fragment read
-// from LDS feeds one MFMA per query block) at the cost of one wave per SIMD.
+// QB = 32-row query blocks per wave, NW = waves per workgroup (32 * QB * NW
+// stacked rows).  QB = 2 would halve the LDS bytes per MFMA (every K and V
+// fragment read from LDS would feed two MFMAs) at one wave per SIMD, but it
+// spills under the compiler's register allocation; the launches use QB = 1.
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
@@ -154,7 +155,6 @@ __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt
 template <int P>
 using Parity = std::integral_constant<int, P>;
 
-//
 // Split-KV mode (part_o != nullptr): the workgroup covers only KV split
 // tc.split -- tiles [s T, min((s + 1) T, all tiles)) with T = ceil(tiles /
 // n_splits), intersected with the causal extent -- and writes the normalised
