@@ -4,7 +4,9 @@ Fused prefill (GQA, causal; split-KV for short query blocks after a long
 prefix), split-KV decode, multi-token decode over a paged KV cache and the
 log-sum-exp combine, as
 hand-written HIP kernels behind the C ABI in ``include/attn.h``.  This package
-is the thin Python binding over ``libattn.so`` plus the seeded workloads.
+is the thin Python binding over ``libattn.so``, the seeded workloads, and
+``sdpa_frontend``, a torch.fx pass that routes attention written in PyTorch to
+the fused kernel.
 """
 
 from ._binding import (  # noqa: F401
@@ -22,3 +24,4 @@ from ._binding import (  # noqa: F401
     splits_for_lengths,
 )
 from . import workloads  # noqa: F401
+from . import sdpa_frontend  # noqa: F401

@@ -1,0 +1,263 @@
+"""The SDPA-pattern front end on the CPU: which graphs it rewrites, which it
+leaves alone and why (shapes propagate on meta tensors; nothing runs)."""
+
+import math
+
+import pytest
+import torch
+import torch.nn.functional as F
+
+from streaming_attention_amd import sdpa_frontend as fe
+
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+class Explicit(torch.nn.Module):
+    def forward(self, q, k, v):
+        s = torch.matmul(q, k.transpose(-2, -1)) / math.sqrt(q.shape[-1])
+        return torch.softmax(s, dim=-1) @ v
+
+
+class ExplicitScaledQ(torch.nn.Module):
+    def forward(self, q, k, v):
+        s = (q * 0.125) @ k.transpose(2, 3)
+        return torch.matmul(F.softmax(s, dim=3), v)
+
+
+class ExplicitUnscaled(torch.nn.Module):
+    def forward(self, q, k, v):
+        return (q @ k.mT).softmax(dim=-1) @ v
+
+
+class Sdpa(torch.nn.Module):
+    def __init__(self, **kw):
+        super().__init__()
+        self.kw = kw
+
+    def forward(self, q, k, v):
+        return F.scaled_dot_product_attention(q, k, v, **self.kw) * 2.0
+
+
+class NotAttention(torch.nn.Module):
+    def forward(self, q, k, v):
+        a = torch.softmax(q @ k.transpose(-2, -1), dim=2) @ v      # softmax over the query axis
+        b = torch.softmax(q @ k, dim=-1)                          # no transpose of K
+        return a, b
+
+
+class BufferCausal(torch.nn.Module):
+    """Causal mask as a lower-triangular module buffer sliced to the sequence length."""
+
+    def __init__(self, n=512):
+        super().__init__()
+        self.register_buffer("tri", torch.tril(torch.ones(n, n)).view(1, 1, n, n))
+
+    def forward(self, q, k, v):
+        T = q.size(2)
+        att = (q @ k.transpose(-2, -1)) * (1.0 / math.sqrt(k.size(-1)))
+        att = att.masked_fill(self.tri[:, :, :T, :T] == 0, float("-inf"))
+        return F.softmax(att, dim=-1) @ v
+
+
+class BottomRightCausal(torch.nn.Module):
+    """Causal mask built in forward, aligned so that the last query sees every key."""
+
+    def forward(self, q, k, v):
+        Sq, Skv = q.shape[2], k.shape[2]
+        hide = q.new_ones(Sq, Skv, dtype=torch.bool).triu(Skv - Sq + 1)
+        s = torch.matmul(q, k.transpose(-2, -1)).masked_fill(hide, float("-inf"))
+        return torch.softmax(s * 0.125, dim=-1) @ v
+
+
+class AdditiveMask(torch.nn.Module):
+    """An added bias buffer (0 where visible, -inf where hidden), after the scale."""
+
+    def __init__(self, bias):
+        super().__init__()
+        self.register_buffer("bias", bias)
+
+    def forward(self, q, k, v):
+        s = q @ k.transpose(-2, -1) / 8.0
+        return torch.softmax(s + self.bias, dim=-1) @ v
+
+
+class DataMask(torch.nn.Module):
+    def forward(self, q, k, v):
+        s = (q @ k.transpose(-2, -1)).masked_fill(k.sum(-1, keepdim=True).transpose(-2, -1) > 0, float("-inf"))
+        return torch.softmax(s, dim=-1) @ v
+
+
+def _additive(Sq, Skv, diag):
+    b = torch.zeros(Sq, Skv)
+    return b.masked_fill(torch.ones(Sq, Skv, dtype=torch.bool).triu(diag), float("-inf"))
+
+
+def test_causal_masks_in_the_chain_are_recognised():
+    q = _t(1, 2, 100, 64)
+    gm, rep = fe.rewrite(BufferCausal(), q, q, q)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": pytest.approx(0.125)}
+    assert not [n for n in gm.graph.nodes if n.op == "get_attr"]          # the mask buffer is no longer read
+    kv = _t(1, 2, 300, 64)
+    gm, rep = fe.rewrite(BottomRightCausal(), q, kv, kv)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": 0.125, "align": "bottom_right"}
+    gm, rep = fe.rewrite(AdditiveMask(_additive(100, 300, 1)), q, kv, kv)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": 0.125}                   # top-left
+    gm, rep = fe.rewrite(AdditiveMask(_additive(100, 300, 201).view(1, 1, 100, 300)), q, kv, kv)
+    (call,) = _calls(gm)
+    assert call.kwargs["align"] == "bottom_right"
+
+
+@pytest.mark.parametrize("mod,why", [
+    (AdditiveMask(_additive(100, 300, 2)), "not causal"),                     # off by one diagonal
+    (AdditiveMask(_additive(100, 300, 1) + torch.linspace(-1, 0, 300)), "other than 0 and -inf"),
+    (AdditiveMask(torch.stack([_additive(100, 300, 1), _additive(100, 300, 201)]).view(1, 2, 100, 300)),
+     "not causal"),                                                           # differs between heads
+    (DataMask(), "depends on"),
+])
+def test_other_masks_are_left_alone(mod, why):
+    q, kv = _t(1, 2, 100, 64), _t(1, 2, 300, 64)
+    gm, rep = fe.rewrite(mod, q, kv, kv)
+    assert not _calls(gm)
+    assert len(rep.skipped) == 1 and why in rep.skipped[0][1], rep.skipped
+
+
+def test_masked_fill_with_a_finite_value_is_not_matched():
+    class Finite(torch.nn.Module):
+        def forward(self, q, k, v):
+            hide = q.new_ones(q.shape[2], k.shape[2], dtype=torch.bool).triu(1)
+            return torch.softmax((q @ k.transpose(-2, -1)).masked_fill(hide, -1e4), dim=-1) @ v
+
+    q = _t(1, 2, 64, 64)
+    gm, rep = fe.rewrite(Finite(), q, q, q)
+    assert not _calls(gm) and not rep.rewritten and not rep.skipped
+
+
+def test_one_broadcast_kv_head_is_legal():
+    gm, rep = fe.rewrite(Explicit(), _t(1, 8, 32, 64), _t(1, 1, 32, 64), _t(1, 1, 32, 64))
+    assert len(_calls(gm)) == 1 and not rep.skipped
+
+
+def _calls(gm):
+    return [n for n in gm.graph.nodes if n.op == "call_function" and n.target is fe.fused_attention]
+
+
+@pytest.mark.parametrize("mod,scale", [(Explicit(), 1 / math.sqrt(128)), (ExplicitScaledQ(), 0.125),
+                                       (ExplicitUnscaled(), 1.0)])
+def test_explicit_chains_are_rewritten(mod, scale):
+    q = _t(2, 4, 64, 128)
+    gm, rep = fe.rewrite(mod, q, q, q)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": False, "scale": pytest.approx(scale)}
+    names = {getattr(n.target, "__name__", str(n.target)) for n in gm.graph.nodes if n.op != "placeholder"}
+    assert "softmax" not in names and "matmul" not in names
+    assert len(rep.rewritten) == 1 and not rep.skipped
+
+
+def test_sdpa_calls_are_rewritten_with_their_flags():
+    q, k = _t(1, 8, 64, 128), _t(1, 2, 64, 128)
+    gm, rep = fe.rewrite(Sdpa(is_causal=True, enable_gqa=True), q, k, k)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": pytest.approx(1 / math.sqrt(128))}
+    gm, _ = fe.rewrite(Sdpa(scale=0.5), q, q, q)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": False, "scale": 0.5}
+
+
+@pytest.mark.parametrize("mod,shapes,dtype,why", [
+    (Explicit(), [(1, 2, 16, 96)] * 3, torch.bfloat16, "head dim"),
+    (Explicit(), [(1, 2, 16, 64)] * 3, torch.float16, "dtype"),
+    (Explicit(), [(2, 16, 64)] * 3, torch.bfloat16, "[B, H, S, d]"),
+    (Sdpa(is_causal=True), [(1, 2, 32, 64), (1, 2, 16, 64), (1, 2, 16, 64)], torch.bfloat16, "more queries"),
+    (Explicit(), [(1, 2, 16, 128), (1, 2, 16, 128), (1, 2, 16, 64)], torch.bfloat16, "K / V shapes"),
+])
+def test_illegal_matches_are_left_alone(mod, shapes, dtype, why):
+    args = [_t(*s, dtype=dtype) for s in shapes]
+    gm, rep = fe.rewrite(mod, *args)
+    assert not _calls(gm)
+    assert len(rep.skipped) == 1 and why in rep.skipped[0][1]
+
+
+def test_masked_or_dropout_sdpa_and_other_softmaxes_are_not_matched():
+    q = _t(1, 2, 16, 64)
+    gm, rep = fe.rewrite(Sdpa(attn_mask=None, dropout_p=0.1), q, q, q)
+    assert not _calls(gm) and not rep.rewritten
+    q = _t(1, 2, 16, 16)
+    gm, rep = fe.rewrite(NotAttention(), q, q, q)
+    assert not _calls(gm) and not rep.rewritten and not rep.skipped
+
+
+# ---- GPU: the rewritten modules against the float64 oracle -------------------------------------------------
+# The original modules never run on the GPU: only their rewritten graphs, from which every matmul, transpose
+# and softmax of the matched region has been removed.
+
+def _gpu_inputs(seed, shapes, dtype):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return [torch.randn(s, generator=g, device="cuda").to(dtype) for s in shapes]
+
+
+def _run_rewritten(mod, args):
+    gm, rep = fe.rewrite(mod, *args)
+    assert len(_calls(gm)) == 1 and not rep.skipped
+    left = {getattr(n.target, "__name__", str(n.target)) for n in gm.graph.nodes if n.op != "placeholder"}
+    assert not left & {"matmul", "softmax", "transpose", "scaled_dot_product_attention"}, left
+    out = gm(*args)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mod,shapes,dtype,scale", [
+    (Explicit(), [(1, 4, 200, 128)] * 3, torch.bfloat16, 1 / math.sqrt(128)),
+    (ExplicitScaledQ(), [(2, 2, 130, 64)] * 3, torch.float32, 0.125),
+    (Explicit(), [(1, 8, 96, 64), (1, 1, 300, 64), (1, 1, 300, 64)], torch.bfloat16, 1 / 8.0),
+])
+def test_rewritten_explicit_chain_matches_oracle(mod, shapes, dtype, scale):
+    import oracle
+    from parity import assert_o, f64
+
+    q, k, v = _gpu_inputs(11, shapes, dtype)
+    o = _run_rewritten(mod, [q, k, v])
+    O_ref, _ = oracle.attention(f64(q), f64(k), f64(v), scale, False)
+    assert_o(o, O_ref, "bf16" if dtype == torch.bfloat16 else "f32")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("Sq,Skv,kw", [
+    (150, 150, dict(is_causal=True, enable_gqa=True)),
+    (100, 300, dict(is_causal=True, enable_gqa=True)),          # top-left causal: the first Sq keys
+    (100, 300, dict(scale=0.05, enable_gqa=True)),
+])
+def test_rewritten_sdpa_matches_oracle(Sq, Skv, kw):
+    import oracle
+    from parity import assert_o, f64
+
+    q, k, v = _gpu_inputs(12, [(1, 8, Sq, 128), (1, 2, Skv, 128), (1, 2, Skv, 128)], torch.bfloat16)
+    o = _run_rewritten(Sdpa(**kw), [q, k, v])
+    causal = kw.get("is_causal", False)
+    scale = kw.get("scale", 1 / math.sqrt(128))
+    n = Sq if causal else Skv       # a top-left causal mask hides every key at or past position Sq
+    O_ref, _ = oracle.attention(f64(q), f64(k)[:, :, :n], f64(v)[:, :, :n], scale, causal)
+    assert_o(o, 2.0 * O_ref, "bf16")          # the module doubles the attention output
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mod,Sq,Skv,top_left", [
+    (BufferCausal(), 200, 200, True),
+    (BottomRightCausal(), 100, 300, False),
+    (AdditiveMask(_additive(100, 300, 1)), 100, 300, True),
+])
+def test_rewritten_masked_chain_matches_oracle(mod, Sq, Skv, top_left):
+    import oracle
+    from parity import assert_o, f64
+
+    mod = mod.cuda()
+    q, k, v = _gpu_inputs(13, [(2, 4, Sq, 64), (2, 4, Skv, 64), (2, 4, Skv, 64)], torch.bfloat16)
+    o = _run_rewritten(mod, [q, k, v])
+    n = Sq if top_left else Skv
+    O_ref, _ = oracle.attention(f64(q), f64(k)[:, :, :n], f64(v)[:, :, :n], 0.125, True)
+    assert_o(o, O_ref, "bf16")
