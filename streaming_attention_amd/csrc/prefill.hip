@@ -459,7 +459,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   };
 
   // One pipelined step, three tiles deep:
-  //   P1  tile kt: mask (straddling / tail tiles only); on the first tile, m;
+  //   P1  tile kt: mask (straddling / tail tiles only);
   //   P2  the score MFMAs of tile kt + 1 (K slot Kn) and the P V MFMAs of tile
   //       kt - 1 (V slot Vp, operand pf_prev) alternate, interleaved with the
   //       exponentials, row sums and bf16 packing of tile kt;
@@ -470,8 +470,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
                   bf16x8 (&pf_new)[QB][2][2], const lds_t* Kn, const lds_t* Vp) {
     const int key_end = kt * kBN + kBN - 1;
     const bool need_mask = (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
-    if (need_mask) mask_tile(kt, S);
-    if (kt == kt_lo) raise_base(S);   // O and l are still zero: this only sets m
+    // A real branch (most tiles need no mask): without the hint the compiler
+    // turns the rare mask into selects executed on every tile.
+    if (__builtin_expect(need_mask, 0)) mask_tile(kt, S);
 
     // P2.  The wave raises its issue priority while it feeds the matrix core,
     // so the arbiter prefers its MFMAs over the other wave's VALU.
@@ -557,6 +558,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     if (wave_active) {
 #pragma unroll
       for (int i = 0; i < 2 * DS; ++i) score_mfma(kbuf[0], sA, i);
+      // The exponent base: the first tile's row max, taken here, outside the
+      // loop, so that the steady-state step carries no max and no rescale.
+      const int key_end = kt_lo * kBN + kBN - 1;
+      if ((key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin)) mask_tile(kt_lo, sA);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m_run[qb] = tile_max(sA[qb]);
     }
     __syncthreads();   // K slot 0 is reloaded in iteration 0
   }
