@@ -52,6 +52,7 @@ constexpr int kNumCUs = 256;          // MI355X compute units
 constexpr float kSumCap = 16777216.f;  // 2^24: largest partial row sum of P accepted without
                                       // raising the exponent base (P <= 2^24 keeps O far from fp32 overflow)
 constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
+constexpr int kRankMax = 256;         // paged mode: most sequences ordered by length
 
 struct TileCoord {
   int b, kvh, mt, split;
@@ -203,11 +204,31 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   const int rows_total = G * Sq;
   const int n_mt = (rows_total + BM - 1) / BM;
   const int n_groups = B * Hkv;
-  const TileCoord tc = map_tile<BM>(blockIdx.x, n_groups * n_splits, n_splits, Hkv, n_mt, G, Sq);
+  TileCoord tc = map_tile<BM>(blockIdx.x, n_groups * n_splits, n_splits, Hkv, n_mt, G, Sq);
   const int r0 = tc.mt * BM;
-  if constexpr (PAGED) {   // keys of this workgroup's sequence
-    const int len = kv_len[tc.b];
-    Skv = len < 0 ? 0 : (len > kBN * max_pages ? kBN * max_pages : len);
+  if constexpr (PAGED) {
+    auto clamp_len = [&](int len) { return len < 0 ? 0 : (len > kBN * max_pages ? kBN * max_pages : len); };
+    // Longest sequences first: map_tile deals the sequence slots in launch
+    // order, and slot r goes to the sequence of rank r by length (ties by
+    // index), so the workgroups with the most tiles start first and the short
+    // ones fill the tail.  Up to kRankMax sequences (beyond that, launch
+    // order); the lengths are staged in LDS and every thread ranks its
+    // sequences against all of them.
+    if (B <= kRankMax) {
+      __shared__ int len_s[kRankMax];
+      __shared__ int pick;
+      for (int j = threadIdx.x; j < B; j += NT) len_s[j] = clamp_len(kv_len[j]);
+      __syncthreads();
+      for (int j = threadIdx.x; j < B; j += NT) {
+        const int lj = len_s[j];
+        int rank = 0;
+        for (int i = 0; i < B; ++i) rank += (len_s[i] > lj) || (len_s[i] == lj && i < j);
+        if (rank == tc.b) pick = j;
+      }
+      __syncthreads();
+      tc.b = __builtin_amdgcn_readfirstlane(pick);
+    }
+    Skv = clamp_len(kv_len[tc.b]);   // keys of this workgroup's sequence
   }
   const int q_start = Skv - Sq;
 

@@ -50,6 +50,9 @@ SMALL = [
     (1, 64, 8, 16, [2000], 128, 4),          # 128 stacked rows: one full row block
     (1, 64, 8, 20, [700], 128, None),        # 160 rows: two row blocks
     (2, 4, 1, 3, [0, 129], 64, 2),           # an empty sequence
+    (5, 8, 2, 2, [200, 64, 200, 64, 200], 128, 2),   # tied lengths (the longest-first order breaks ties by index)
+    (256, 4, 1, 2, [(37 * i) % 190 for i in range(256)], 64, 2),   # most sequences the in-kernel order ranks
+    (300, 4, 1, 2, [(53 * i) % 170 for i in range(300)], 64, 2),   # more: launch order
 ]
 
 
