@@ -19,6 +19,10 @@ the host cores on a bounded sample of the same prefill workload, is reported as
 `cpu_baseline` (a baseline only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Defaults: 20 warmup steps, 30 timed.  The GPU's clock settles only after some
+tens of milliseconds of this load: in a kernel trace the prefill's first
+launches take up to 1.2 ms and later ones 0.98 ms.
 """
 
 from __future__ import annotations
@@ -37,21 +41,23 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQA"
 
 # Measured HBM bytes per launch of the dominant kernels: two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) on `bench.py --only prefill|decode`,
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) on `bench.py --only prefill|decode|chunked|paged`,
 # each scaled by what the same counter reads for a plain 1 GiB device copy
 # (`bench.py --only copy`: FETCH_SIZE reads 0.5x the copied bytes, WRITE_SIZE 1.0x).
 # Each entry holds for the kernel sources whose hash it records; after any change to
 # them the bench reports traffic as null until the counters are taken again.
-# Summary and commands: profiles/hbm_traffic_70b_prefill_decode_chunked.md.
+# Summary and commands: profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "17a11adc1ce6e20e",
-                "fetch_kib": 138465, "write_kib": 133120},
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "146e8777165c5387",
+                "fetch_kib": 138354, "write_kib": 133120},
     "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "0d37c578dc2e19f6",
                "fetch_kib": 262478 + 4172, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "8181934023498632",
-                "fetch_kib": 140882 + 16917, "write_kib": 33280 + 8448},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "c92164c6109165b1",
+                "fetch_kib": 140585 + 16917, "write_kib": 33280 + 8448},
+    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "c92164c6109165b1",
+              "fetch_kib": 592146 + 8278, "write_kib": 17409 + 1056},
 }
 
 
@@ -71,8 +77,8 @@ def measured_traffic(name):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "chunked", "paged", "copy"], default="all",
                     help="run only one part (for per-kernel profiling runs): one half of the step, the "
@@ -256,7 +262,9 @@ def main():
                  "kv_splits": n_sp,
                  "kernels": "prefill_bf16_kernel<128,causal,paged> (split-KV) + combine_lse",
                  "us": round(pg_ms * 1e3, 2), "kv_gbs": round(pg_gbs, 1),
-                 "pct_hbm_peak": round(100 * pg_gbs / HBM_PEAK_GBS, 2), "kv_bytes": pg_bytes}
+                 "pct_hbm_peak": round(100 * pg_gbs / HBM_PEAK_GBS, 2), "kv_bytes": pg_bytes,
+                 "traffic": measured_traffic("paged"),
+                 "traffic_unit": "HBM bytes per call, paged split-KV + merge (fetch + write)"}
         del qg, kpg, vpg, tbl_d, lens_d, og, lseg
 
     pf_flops = wp.flops()
