@@ -130,7 +130,9 @@ def _is_matmul(n) -> bool:
                                        or (n.op == "call_method" and n.target == "matmul"))
 
 
-def _softmax_last_dim(n) -> fx.Node | None:
+def _softmax_last_dim(n, gm=None) -> fx.Node | None:
+    """The scores node if n is a softmax over the last dim (function, method
+    or an ``nn.Softmax`` submodule), else None."""
     if not isinstance(n, fx.Node):
         return None
     dim = None
@@ -138,6 +140,8 @@ def _softmax_last_dim(n) -> fx.Node | None:
         dim = n.kwargs.get("dim", n.args[1] if len(n.args) > 1 else None)
     elif n.op == "call_method" and n.target == "softmax":
         dim = n.kwargs.get("dim", n.args[1] if len(n.args) > 1 else None)
+    elif n.op == "call_module" and gm is not None and isinstance(_fetch_attr(gm, n.target), torch.nn.Softmax):
+        dim = _fetch_attr(gm, n.target).dim
     else:
         return None
     return n.args[0] if dim in (-1, 3) else None
@@ -292,7 +296,7 @@ def find_attention(gm: fx.GraphModule) -> list[Match]:
             found.append(Match(args[0], args[1], args[2], None if scale is None else float(scale), causal, n,
                                "sdpa", gqa))
             continue
-        scores = _softmax_last_dim(n)
+        scores = _softmax_last_dim(n, gm)
         if scores is None or not _single_user(n):
             continue
         pv = next(iter(n.users))

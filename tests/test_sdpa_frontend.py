@@ -137,6 +137,25 @@ def test_masked_fill_with_a_finite_value_is_not_matched():
     assert not _calls(gm) and not rep.rewritten and not rep.skipped
 
 
+class SoftmaxModule(torch.nn.Module):
+    """The softmax as an nn.Softmax submodule (a leaf of the trace)."""
+
+    def __init__(self):
+        super().__init__()
+        self.softmax = torch.nn.Softmax(dim=-1)
+
+    def forward(self, q, k, v):
+        return torch.matmul(self.softmax(torch.matmul(q, k.transpose(-1, -2)) * 0.125), v)
+
+
+def test_softmax_submodule_is_matched():
+    q = _t(1, 2, 48, 64)
+    gm, rep = fe.rewrite(SoftmaxModule(), q, q, q)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": False, "scale": 0.125}
+    assert not [n for n in gm.graph.nodes if n.op == "call_module"]
+
+
 def test_one_broadcast_kv_head_is_legal():
     gm, rep = fe.rewrite(Explicit(), _t(1, 8, 32, 64), _t(1, 1, 32, 64), _t(1, 1, 32, 64))
     assert len(_calls(gm)) == 1 and not rep.skipped
