@@ -16,7 +16,13 @@ region):
   shapes only; its values are evaluated once at rewrite time and accepted when
   they are exactly a causal mask ("AI Compiler pipeline stages", Pattern
   Matching: ``MatMul(Q, K^T) -> Mask(causal) -> Softmax``), aligned top-left
-  (query t sees keys 0..t) or bottom-right (query t sees keys 0..Skv-Sq+t);
+  (query t sees keys 0..t) or bottom-right (query t sees keys 0..Skv-Sq+t).
+  Between the softmax and the P V product, casts, ``contiguous`` and dropout
+  that is off (p = 0, or not training at rewrite time) are passed over.  K and
+  V repeated along the head dim for grouped-query attention
+  (``repeat_interleave(G, dim=1)``, or the unsqueeze-expand-reshape idiom)
+  are matched back to the unrepeated tensors, which the kernel reads once per
+  KV head;
 * legality, from shapes and dtypes propagated on meta tensors: 4-D
   ``[B, H, S, d]`` operands of one dtype (bf16 or fp32), d 64 or 128, query
   heads a multiple of KV heads (broadcast or ``enable_gqa``), and for causal
@@ -70,7 +76,7 @@ class Match:
     causal: bool
     out: fx.Node             # node whose uses the fused call takes over
     kind: str                # "explicit" or "sdpa"
-    gqa: bool = False        # SDPA's enable_gqa
+    gqa: bool = False        # SDPA's enable_gqa, or K / V repeats matched away
     align: str = "top_left"  # causal mask alignment: "top_left" or "bottom_right"
     mask_error: str | None = None   # why a mask in the chain is not a causal mask
 
@@ -279,6 +285,68 @@ def _mask_alignment(gm, mask_node, how, Sq, Skv) -> tuple[str | None, str | None
     return (align, None) if align else (None, "mask is not causal")
 
 
+def _passes_probabilities(n, gm) -> bool:
+    """True for a node that hands the probabilities on unchanged up to
+    rounding to the P V product's dtype: a cast, ``contiguous``, or dropout
+    that is off."""
+    if n.op == "call_method" and n.target in ("to", "type", "type_as", "contiguous"):
+        return True
+    if n.op == "call_function" and n.target is torch.nn.functional.dropout:
+        p = n.kwargs.get("p", n.args[1] if len(n.args) > 1 else 0.5)
+        training = n.kwargs.get("training", n.args[2] if len(n.args) > 2 else True)
+        return p == 0 or training is False
+    if n.op == "call_module":
+        mod = _fetch_attr(gm, n.target)
+        return isinstance(mod, torch.nn.Dropout) and (mod.p == 0 or not mod.training)
+    return False
+
+
+def _unsqueezed_at_2(n) -> fx.Node | None:
+    """x if n is x.unsqueeze(2) or x[:, :, None] (x 4-D), else None."""
+    if not isinstance(n, fx.Node):
+        return None
+    if n.op == "call_method" and n.target == "unsqueeze" and len(n.args) == 2 and n.args[1] == 2:
+        return n.args[0]
+    if n.op == "call_function" and n.target is torch.unsqueeze and len(n.args) == 2 and n.args[1] == 2:
+        return n.args[0]
+    if n.op == "call_function" and n.target is operator.getitem and isinstance(n.args[1], tuple):
+        idx = n.args[1]
+        full = slice(None, None, None)
+        if len(idx) >= 3 and idx[0] == full and idx[1] == full and idx[2] is None and \
+                all(i == full or i is Ellipsis for i in idx[3:]):
+            return n.args[0]
+    return None
+
+
+def _strip_kv_repeat(n):
+    """(x, G) when n is x with every head repeated G times in a row along dim
+    1 -- ``repeat_interleave(G, dim=1)`` or ``x[:, :, None].expand(B, H, G, S,
+    d).reshape(B, H * G, S, d)`` -- so that head h of n is head h // G of x;
+    else (n, 1).  Shapes come from shape propagation."""
+    if not isinstance(n, fx.Node):
+        return n, 1
+    if (n.op == "call_method" and n.target == "repeat_interleave") or \
+            (n.op == "call_function" and n.target is torch.repeat_interleave):
+        reps = _const(n.kwargs.get("repeats", n.args[1] if len(n.args) > 1 else None))
+        dim = n.kwargs.get("dim", n.args[2] if len(n.args) > 2 else None)
+        if isinstance(reps, int) and reps >= 1 and dim in (1, -3):
+            return n.args[0], reps
+        return n, 1
+    if n.op == "call_method" and n.target in ("reshape", "view") and isinstance(n.args[0], fx.Node):
+        ex = n.args[0]
+        if ex.op != "call_method" or ex.target != "expand":
+            return n, 1
+        x = _unsqueezed_at_2(ex.args[0])
+        tx, te, tn = _meta(x), _meta(ex), _meta(n)
+        if x is None or tx is None or te is None or tn is None:
+            return n, 1
+        xs, es, ns = tuple(tx.shape), tuple(te.shape), tuple(tn.shape)
+        if len(xs) == 4 and len(es) == 5 and len(ns) == 4 and es[:2] == xs[:2] and es[3:] == xs[2:] and \
+                ns == (xs[0], xs[1] * es[2], xs[2], xs[3]):
+            return x, es[2]
+    return n, 1
+
+
 def find_attention(gm: fx.GraphModule) -> list[Match]:
     """Pattern matching: every explicit softmax(mask?(QK^T)) V chain and SDPA call."""
     found = []
@@ -299,8 +367,13 @@ def find_attention(gm: fx.GraphModule) -> list[Match]:
         scores = _softmax_last_dim(n, gm)
         if scores is None or not _single_user(n):
             continue
-        pv = next(iter(n.users))
-        if not _is_matmul(pv) or pv.args[0] is not n:
+        probs = n                          # last node before the P V product
+        while _single_user(probs) and _passes_probabilities(next(iter(probs.users)), gm):
+            probs = next(iter(probs.users))
+        if not _single_user(probs):
+            continue
+        pv = next(iter(probs.users))
+        if not _is_matmul(pv) or pv.args[0] is not probs:
             continue
         chain = [scores]                   # nodes between the score product and the softmax
         inner, f1 = _strip_scale(scores)
@@ -318,7 +391,12 @@ def find_attention(gm: fx.GraphModule) -> list[Match]:
         kn = _is_last2_transpose(inner.args[1])
         if kn is None:
             continue
-        m = Match(qn, kn, pv.args[1], f1 * f2 * f3, mask_node is not None, pv, "explicit")
+        vn = pv.args[1]
+        kb, gk = _strip_kv_repeat(kn)
+        vb, gv = _strip_kv_repeat(vn)
+        if gk == gv and gk > 1:            # grouped-query attention written with repeated K / V
+            kn, vn = kb, vb
+        m = Match(qn, kn, vn, f1 * f2 * f3, mask_node is not None, pv, "explicit", gqa=(gk == gv and gk > 1))
         if mask_node is not None:
             tq, tk = _meta(qn), _meta(kn)
             if tq is None or tk is None or len(tq.shape) < 2 or len(tk.shape) < 2:
@@ -354,8 +432,8 @@ def legality(m: Match) -> str | None:
         return f"head dim {d}"
     if Bk != B or Hq % Hkv != 0:
         return "batch or head counts"
-    if Hq != Hkv and not (m.gqa if m.kind == "sdpa" else Hkv == 1):
-        return "query and KV head counts differ without grouping (enable_gqa, or one broadcast KV head)"
+    if Hq != Hkv and not (m.gqa or (m.kind == "explicit" and Hkv == 1)):
+        return "query and KV head counts differ without grouping (enable_gqa, repeated K / V, or one KV head)"
     if m.causal and Sq > Skv:
         return "causal with more queries than keys (some rows would see no key)"
     return None

@@ -156,6 +156,65 @@ def test_softmax_submodule_is_matched():
     assert not [n for n in gm.graph.nodes if n.op == "call_module"]
 
 
+def _repeat_kv(x, n_rep):
+    """Grouped-query K / V repeated along the head dim (expand + reshape)."""
+    b, h, s_, d = x.shape
+    return x[:, :, None, :, :].expand(b, h, n_rep, s_, d).reshape(b, h * n_rep, s_, d)
+
+
+class LlamaStyle(torch.nn.Module):
+    """Eager grouped-query attention as transformer code often writes it: K / V
+    repeated per query head, fp32 softmax cast back, dropout that is off."""
+
+    def __init__(self, n_rep, causal_len=None):
+        super().__init__()
+        self.n_rep = n_rep
+        self.drop = torch.nn.Dropout(0.1)
+        if causal_len:
+            self.register_buffer("tri", torch.tril(torch.ones(causal_len, causal_len, dtype=torch.bool)))
+        else:
+            self.tri = None
+
+    def forward(self, q, k, v):
+        k = _repeat_kv(k, self.n_rep)
+        v = _repeat_kv(v, self.n_rep)
+        w = torch.matmul(q, k.transpose(2, 3)) * (q.shape[-1] ** -0.5)
+        if self.tri is not None:
+            T = q.shape[2]
+            w = w.masked_fill(~self.tri[:T, :T], float("-inf"))
+        w = F.softmax(w, dim=-1, dtype=torch.float32).to(q.dtype)
+        w = F.dropout(w, p=0.1, training=False)
+        w = self.drop(w)
+        return torch.matmul(w, v).transpose(1, 2).contiguous()
+
+
+class RepeatInterleave(torch.nn.Module):
+    def forward(self, q, k, v):
+        k = k.repeat_interleave(4, dim=1)
+        v = torch.repeat_interleave(v, 4, dim=1)
+        return torch.softmax(q @ k.transpose(-2, -1) * 0.125, dim=-1) @ v
+
+
+@pytest.mark.parametrize("mod,causal", [(LlamaStyle(4).eval(), False), (LlamaStyle(4, 256).eval(), True),
+                                        (RepeatInterleave(), False)])
+def test_repeated_kv_heads_are_read_once(mod, causal):
+    q, kv = _t(1, 8, 96, 64), _t(1, 2, 96, 64)
+    gm, rep = fe.rewrite(mod, q, kv, kv)
+    (call,) = _calls(gm)
+    assert [a.name for a in call.args] == ["q", "k", "v"]          # the unrepeated K and V
+    assert call.kwargs["causal"] is causal and call.kwargs["scale"] == pytest.approx(0.125)
+    left = {getattr(n.target, "__name__", str(n.target)) for n in gm.graph.nodes if n.op in ("call_method",
+                                                                                             "call_function")}
+    assert not left & {"expand", "reshape", "repeat_interleave", "softmax", "dropout", "matmul"}, left
+
+
+def test_dropout_in_training_is_not_passed_over():
+    mod = LlamaStyle(4).train()
+    q, kv = _t(1, 8, 32, 64), _t(1, 2, 32, 64)
+    gm, rep = fe.rewrite(mod, q, kv, kv)
+    assert not _calls(gm) and not rep.rewritten
+
+
 def test_one_broadcast_kv_head_is_legal():
     gm, rep = fe.rewrite(Explicit(), _t(1, 8, 32, 64), _t(1, 1, 32, 64), _t(1, 1, 32, 64))
     assert len(_calls(gm)) == 1 and not rep.skipped
@@ -211,8 +270,8 @@ def test_masked_or_dropout_sdpa_and_other_softmaxes_are_not_matched():
 
 
 # ---- GPU: the rewritten modules against the float64 oracle -------------------------------------------------
-# The original modules never run on the GPU: only their rewritten graphs, from which every matmul, transpose
-# and softmax of the matched region has been removed.
+# The original modules never run on the GPU: only their rewritten graphs, from which every matmul and softmax
+# of the matched region has been removed (no batched bf16 product with a transposed operand runs).
 
 def _gpu_inputs(seed, shapes, dtype):
     g = torch.Generator(device="cuda").manual_seed(seed)
@@ -223,7 +282,7 @@ def _run_rewritten(mod, args):
     gm, rep = fe.rewrite(mod, *args)
     assert len(_calls(gm)) == 1 and not rep.skipped
     left = {getattr(n.target, "__name__", str(n.target)) for n in gm.graph.nodes if n.op != "placeholder"}
-    assert not left & {"matmul", "softmax", "transpose", "scaled_dot_product_attention"}, left
+    assert not left & {"matmul", "bmm", "softmax", "scaled_dot_product_attention"}, left
     out = gm(*args)
     torch.cuda.synchronize()
     return out
@@ -262,6 +321,19 @@ def test_rewritten_sdpa_matches_oracle(Sq, Skv, kw):
     n = Sq if causal else Skv       # a top-left causal mask hides every key at or past position Sq
     O_ref, _ = oracle.attention(f64(q), f64(k)[:, :, :n], f64(v)[:, :, :n], scale, causal)
     assert_o(o, 2.0 * O_ref, "bf16")          # the module doubles the attention output
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("causal", [False, True])
+def test_rewritten_llama_style_gqa_matches_oracle(causal):
+    import oracle
+    from parity import assert_o, f64
+
+    mod = LlamaStyle(4, 512 if causal else None).eval().cuda()
+    q, k, v = _gpu_inputs(14, [(2, 16, 200, 128), (2, 4, 200, 128), (2, 4, 200, 128)], torch.bfloat16)
+    o = _run_rewritten(mod, [q, k, v])
+    O_ref, _ = oracle.attention(f64(q), f64(k), f64(v), 128 ** -0.5, causal)
+    assert_o(o, O_ref.transpose(0, 2, 1, 3), "bf16")
 
 
 @pytest.mark.gpu
