@@ -50,26 +50,35 @@ METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQ
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "146e8777165c5387",
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "2c3f282679bdf139",
                 "fetch_kib": 138354, "write_kib": 133120},
-    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "0d37c578dc2e19f6",
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "6d10173e6e4bd89b",
                "fetch_kib": 262478 + 4172, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "c92164c6109165b1",
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "40dd65eb06df6354",
                 "fetch_kib": 140585 + 16917, "write_kib": 33280 + 8448},
-    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "c92164c6109165b1",
+    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "40dd65eb06df6354",
               "fetch_kib": 592146 + 8278, "write_kib": 17409 + 1056},
 }
 
 
+def code_hash(sources):
+    """First 16 hex digits of the SHA-256 of the kernel sources' code: each
+    file with its // comments, trailing blanks and empty lines removed, so that
+    a comment edit does not retire the counters."""
+    import hashlib
+    import re
+    m = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "streaming_attention_amd", "csrc", f), encoding="utf-8") as fh:
+            text = re.sub(r"//[^\n]*", "", fh.read())
+        m.update("\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip()).encode())
+    return m.hexdigest()[:16]
+
+
 def measured_traffic(name):
     """HBM bytes per launch (fetch + write, copy-calibrated), or None if stale."""
-    import hashlib
     t = TRAFFIC[name]
-    m = hashlib.sha256()
-    for f in t["sources"]:
-        with open(os.path.join(ROOT, "streaming_attention_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
-    if m.hexdigest()[:16] != t["sha256_16"]:
+    if code_hash(t["sources"]) != t["sha256_16"]:
         return None
     return int(t["fetch_kib"] * 1024 / FETCH_SCALE + t["write_kib"] * 1024 / WRITE_SCALE)
 

@@ -10,11 +10,13 @@
 // streamed HBM -> shared memory -> registers, S and P never written out.
 //
 // MI355X mapping (bf16 path)
-//   * One workgroup = 4 waves = 128 stacked query rows of one (batch, KV head);
-//     each wave owns 32 rows.  KV tiles of 64 keys go from global memory
-//     straight into LDS (buffer loads with the LDS destination, no register
-//     staging), double buffered: the next tiles' loads are in flight while the
-//     current tile is computed, and one barrier per tile orders the rings.
+//   * One workgroup = 8 waves = 256 stacked query rows of one (batch, KV head)
+//     when there are enough such blocks to give every CU one, else 4 waves =
+//     128 rows (two workgroups per CU); each wave owns 32 rows.  KV tiles of
+//     64 keys go from global memory straight into LDS (buffer loads with the
+//     LDS destination, no register staging), double buffered: the next tiles'
+//     loads are in flight while the current tile is computed, and one barrier
+//     per tile orders the rings.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     K (from LDS) is the A operand and Q (held in VGPRs for the whole sweep)
 //     the B operand.  In the accumulator layout every lane then owns ONE query
@@ -29,11 +31,15 @@
 //     movement.  V stays row-major in LDS; the transposing LDS read of gfx950
 //     (ds_read_b64_tr_b16) delivers the matching V^T fragments.
 //   * Softmax runs in base 2: c = scale * log2(e) is folded into one FMA before
-//     v_exp_f32.  Masks are selects to -inf, never additions.
+//     v_exp_f32, against a fixed exponent base per row (the first tile's max,
+//     raised only when a tile's probabilities grow large).  Masks are selects
+//     to -inf, never additions, on straddling and tail tiles only.
 //   * Work order: heaviest causal tiles first, and when the number of
 //     (batch, KV head) groups is a multiple of 8, every group's tiles go to one
 //     XCD (workgroups are dealt to the 8 XCDs round robin) so its K/V stays in
-//     that XCD's L2.
+//     that XCD's L2.  Split-KV mode (a key range per workgroup, fp32 partials)
+//     and paged mode (multi-token decode over a page pool, longest sequences
+//     first) reuse the same loop; see the notes above the kernel.
 //
 // fp32 path: the same loop with v_mfma_f32_32x32x2_f32 (one K value per lane
 // per step, so V needs no transpose) and 32-key tiles, P kept in fp32.
