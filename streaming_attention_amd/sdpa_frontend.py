@@ -10,10 +10,11 @@ region):
 * pattern: ``softmax(mask(scale * (Q @ K^T)), dim=-1) @ V`` written out (the
   scale as a constant multiply or divide of the scores, or of Q, before or
   after the mask; the mask optional), and calls of
-  ``torch.nn.functional.scaled_dot_product_attention`` without an explicit
-  mask or dropout (``is_causal`` allowed).  A mask is ``masked_fill(M, -inf)``
-  or an added bias of 0 / -inf computed from constants, module buffers and
-  shapes only; its values are evaluated once at rewrite time and accepted when
+  ``torch.nn.functional.scaled_dot_product_attention`` without dropout
+  (``is_causal``, or an ``attn_mask`` that is causal).  A mask is
+  ``masked_fill(M, -inf)``, an added bias of 0 / -inf, or SDPA's boolean
+  (keep) or float (bias) ``attn_mask``, computed from constants, module
+  buffers and shapes only; its values are evaluated once at rewrite time and accepted when
   they are exactly a causal mask ("AI Compiler pipeline stages", Pattern
   Matching: ``MatMul(Q, K^T) -> Mask(causal) -> Softmax``), aligned top-left
   (query t sees keys 0..t) or bottom-right (query t sees keys 0..Skv-Sq+t).
@@ -272,11 +273,11 @@ def _mask_alignment(gm, mask_node, how, Sq, Skv) -> tuple[str | None, str | None
         return None, f"mask not evaluable ({type(e).__name__})"
     if not isinstance(val, torch.Tensor):
         return None, "mask is not a tensor"
-    if how == "fill":
-        if val.dtype != torch.bool:
-            return None, "masked_fill mask is not boolean"
-        masked = val
-    else:
+    if how in ("fill", "keep") and val.dtype == torch.bool:
+        masked = val if how == "fill" else ~val
+    elif how == "fill":
+        return None, "masked_fill mask is not boolean"
+    else:                          # an added bias (an explicit add, or SDPA's float mask)
         v = val.double()
         masked = v <= _NEG_INF_LIKE
         if not bool(((v == 0) | masked).all()):
@@ -347,6 +348,18 @@ def _strip_kv_repeat(n):
     return n, 1
 
 
+def _explicit_mask(gm, m: Match, mask_node, how: str) -> None:
+    """Record on m whether mask_node (used as ``how``) is a causal mask, and
+    its alignment; a non-causal mask leaves m illegal with the reason."""
+    tq, tk = _meta(m.q), _meta(m.k)
+    if tq is None or tk is None or len(tq.shape) < 2 or len(tk.shape) < 2:
+        m.mask_error = "no shape information for the mask"
+        return
+    align, why = _mask_alignment(gm, mask_node, how, tq.shape[-2], tk.shape[-2])
+    m.causal = why is None
+    m.align, m.mask_error = (align or "top_left"), why
+
+
 def find_attention(gm: fx.GraphModule) -> list[Match]:
     """Pattern matching: every explicit softmax(mask?(QK^T)) V chain and SDPA call."""
     found = []
@@ -354,15 +367,17 @@ def find_attention(gm: fx.GraphModule) -> list[Match]:
         if n.op == "call_function" and n.target is _SDPA:
             args = list(n.args) + [None] * (3 - len(n.args))
             kw = n.kwargs
-            if kw.get("attn_mask") is not None or (len(n.args) > 3 and n.args[3] is not None):
-                continue
             if kw.get("dropout_p", n.args[4] if len(n.args) > 4 else 0.0) not in (0, 0.0):
                 continue
             causal = bool(kw.get("is_causal", n.args[5] if len(n.args) > 5 else False))
             scale = kw.get("scale", n.args[6] if len(n.args) > 6 else None)
             gqa = bool(kw.get("enable_gqa", False))
-            found.append(Match(args[0], args[1], args[2], None if scale is None else float(scale), causal, n,
-                               "sdpa", gqa))
+            m = Match(args[0], args[1], args[2], None if scale is None else float(scale), causal, n, "sdpa", gqa)
+            attn_mask = kw.get("attn_mask", n.args[3] if len(n.args) > 3 else None)
+            if attn_mask is not None:   # (PyTorch allows no is_causal with it)
+                # SDPA's boolean mask keeps the True entries; a float mask is added to the scores.
+                _explicit_mask(gm, m, attn_mask, "keep")
+            found.append(m)
             continue
         scores = _softmax_last_dim(n, gm)
         if scores is None or not _single_user(n):
@@ -398,12 +413,7 @@ def find_attention(gm: fx.GraphModule) -> list[Match]:
             kn, vn = kb, vb
         m = Match(qn, kn, vn, f1 * f2 * f3, mask_node is not None, pv, "explicit", gqa=(gk == gv and gk > 1))
         if mask_node is not None:
-            tq, tk = _meta(qn), _meta(kn)
-            if tq is None or tk is None or len(tq.shape) < 2 or len(tk.shape) < 2:
-                m.mask_error = "no shape information for the mask"
-            else:
-                align, why = _mask_alignment(gm, mask_node, how, tq.shape[-2], tk.shape[-2])
-                m.align, m.mask_error = (align or "top_left"), why
+            _explicit_mask(gm, m, mask_node, how)
         found.append(m)
     return found
 

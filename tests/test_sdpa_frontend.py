@@ -215,6 +215,45 @@ def test_dropout_in_training_is_not_passed_over():
     assert not _calls(gm) and not rep.rewritten
 
 
+class SdpaMask(torch.nn.Module):
+    """SDPA with an explicit attn_mask buffer (bool: True = keep; float: added)."""
+
+    def __init__(self, mask, **kw):
+        super().__init__()
+        self.register_buffer("mask", mask)
+        self.kw = kw
+
+    def forward(self, q, k, v):
+        return F.scaled_dot_product_attention(q, k, v, attn_mask=self.mask, **self.kw)
+
+
+class SdpaMaskInput(torch.nn.Module):
+    def forward(self, q, k, v, m):
+        return F.scaled_dot_product_attention(q, k, v, attn_mask=m)
+
+
+def test_sdpa_causal_attn_masks_are_recognised():
+    q, kv = _t(1, 2, 100, 64), _t(1, 2, 300, 64)
+    keep = torch.ones(100, 300, dtype=torch.bool).tril()                      # top-left
+    gm, rep = fe.rewrite(SdpaMask(keep), q, kv, kv)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": pytest.approx(0.125)}
+    gm, rep = fe.rewrite(SdpaMask(_additive(100, 300, 201), scale=0.5), q, kv, kv)   # bottom-right, float
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": 0.5, "align": "bottom_right"}
+
+
+@pytest.mark.parametrize("mod,extra,why", [
+    (SdpaMask(torch.ones(100, 300, dtype=torch.bool).tril(1)), [], "not causal"),
+    (SdpaMaskInput(), [torch.ones(100, 300, dtype=torch.bool)], "depends on"),
+])
+def test_other_sdpa_masks_are_left_alone(mod, extra, why):
+    q, kv = _t(1, 2, 100, 64), _t(1, 2, 300, 64)
+    gm, rep = fe.rewrite(mod, q, kv, kv, *extra)
+    assert not _calls(gm)
+    assert len(rep.skipped) == 1 and why in rep.skipped[0][1], rep.skipped
+
+
 def test_one_broadcast_kv_head_is_legal():
     gm, rep = fe.rewrite(Explicit(), _t(1, 8, 32, 64), _t(1, 1, 32, 64), _t(1, 1, 32, 64))
     assert len(_calls(gm)) == 1 and not rep.skipped
@@ -334,6 +373,18 @@ def test_rewritten_llama_style_gqa_matches_oracle(causal):
     o = _run_rewritten(mod, [q, k, v])
     O_ref, _ = oracle.attention(f64(q), f64(k), f64(v), 128 ** -0.5, causal)
     assert_o(o, O_ref.transpose(0, 2, 1, 3), "bf16")
+
+
+@pytest.mark.gpu
+def test_rewritten_sdpa_with_causal_attn_mask_matches_oracle():
+    import oracle
+    from parity import assert_o, f64
+
+    mod = SdpaMask(torch.ones(100, 300, dtype=torch.bool).tril(200), enable_gqa=True).cuda()   # bottom-right
+    q, k, v = _gpu_inputs(15, [(2, 8, 100, 128), (2, 2, 300, 128), (2, 2, 300, 128)], torch.bfloat16)
+    o = _run_rewritten(mod, [q, k, v])
+    O_ref, _ = oracle.attention(f64(q), f64(k), f64(v), 128 ** -0.5, True)
+    assert_o(o, O_ref, "bf16")
 
 
 @pytest.mark.gpu
