@@ -119,3 +119,15 @@ def test_paged_decode_per_sequence_splits(kps):
     o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), scale=w.scale, keys_per_split=kps)
     torch.cuda.synchronize()
     _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(4))
+
+
+@pytest.mark.parametrize("T_q,d,lens", [(32, 128, [3000, 257, 1999, 64]), (20, 64, [700, 20, 1500, 5])])
+def test_paged_decode_eight_wave_launch(T_q, d, lens):
+    """Query blocks of more than 128 stacked rows with enough workgroups: the 8-wave paged kernel."""
+    B, Hq, Hkv, n = 4, 64, 8, 8
+    assert (Hq // Hkv) * T_q > 128 and -(-(Hq // Hkv) * T_q // 256) * B * Hkv * n >= 256
+    w = dataclasses.replace(W.PAGED_DECODE, B=B, Hq=Hq, Hkv=Hkv, T_q=T_q, d=d, seed=500 + T_q)
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=torch.tensor(lens))
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=n, scale=w.scale)
+    torch.cuda.synchronize()
+    _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(B))

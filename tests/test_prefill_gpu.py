@@ -306,6 +306,7 @@ EIGHT_WAVE = [
     (1, 32, 32, 2048, 2048, 64, False),
     (1, 64, 8, 1024, 1500, 128, False),
     (2, 16, 2, 2048, 2048, 64, True),
+    (2, 40, 8, 1000, 1000, 128, True),     # G = 5: row blocks straddle query heads, ragged last block
 ]
 
 
