@@ -213,3 +213,19 @@ def test_fused_small_decode(B, Hq, Hkv, S_cap, d, lens, nsplits, max_splits):
                                                f64(v[b:b + 1, :, :n]), [n], scale)
         assert_o(o[b, :, 0], O_ref[0], "bf16")
         assert_lse(lse[b], L_ref[0], "bf16")
+
+
+def test_out_of_range_lengths_and_split_counts_are_clamped():
+    """kv_len and num_splits are device data the host cannot check: lengths
+    act as clamped to [0, S_cap], split counts to [1, max_splits]."""
+    B, Hq, Hkv, S_cap, d, max_splits = 4, 8, 2, 300, 128, 4
+    g = torch.Generator(device=DEV).manual_seed(4242)
+    q = torch.randn((B, Hq, 1, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    lens = torch.tensor([-5, S_cap + 100, 10, 299], dtype=torch.int32, device=DEV)
+    ns = torch.tensor([0, 999, 2, -3], dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(d)
+    o, lse = sa.decode(q, k, v, lens, ns, max_splits, scale=scale)
+    torch.cuda.synchronize()
+    _check_rows(o, lse, q, k, v, [0, S_cap, 10, 299], scale, range(B))

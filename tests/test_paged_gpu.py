@@ -2,6 +2,7 @@
 tokens per sequence over a paged, shuffled KV cache with ragged lengths."""
 
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -131,3 +132,22 @@ def test_paged_decode_eight_wave_launch(T_q, d, lens):
     o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=n, scale=w.scale)
     torch.cuda.synchronize()
     _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(B))
+
+
+def test_out_of_range_table_entries_and_lengths_are_clamped():
+    """Block-table entries outside the pool act as clamped into [0, num_pages)
+    and lengths as clamped to max_pages pages (device data the host cannot
+    check)."""
+    B, Hq, Hkv, T_q, d, num_pages = 2, 8, 2, 2, 64, 6
+    g = torch.Generator(device=DEV).manual_seed(4343)
+    q = torch.randn((B, Hq, T_q, d), generator=g, device=DEV).to(torch.bfloat16)
+    kp = torch.randn((num_pages, Hkv, 64, d), generator=g, device=DEV).to(torch.bfloat16)
+    vp = torch.randn((num_pages, Hkv, 64, d), generator=g, device=DEV).to(torch.bfloat16)
+    table = torch.tensor([[1, 4, -7], [99, 2, 3]], dtype=torch.int32)
+    lens = torch.tensor([150, 10000], dtype=torch.int32)
+    scale = 1 / math.sqrt(d)
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), num_splits=2, scale=scale)
+    torch.cuda.synchronize()
+    table_eff = table.clamp(0, num_pages - 1)
+    lens_eff = lens.clamp(max=3 * 64)
+    _check(o, lse, q, kp, vp, table_eff, lens_eff, scale, range(B))
