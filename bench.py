@@ -52,12 +52,12 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "2c3f282679bdf139",
                 "fetch_kib": 138354, "write_kib": 133120},
-    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "6d10173e6e4bd89b",
-               "fetch_kib": 262478 + 4172, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "40dd65eb06df6354",
-                "fetch_kib": 140585 + 16917, "write_kib": 33280 + 8448},
-    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "40dd65eb06df6354",
-              "fetch_kib": 592146 + 8278, "write_kib": 17409 + 1056},
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "e2f749b667918352",
+               "fetch_kib": 262472 + 4174, "write_kib": 8704 + 72},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "068b81e27a31b0cc",
+                "fetch_kib": 140591 + 16917, "write_kib": 33282 + 8448},
+    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "068b81e27a31b0cc",
+              "fetch_kib": 592147 + 8278, "write_kib": 17410 + 1056},
 }
 
 

@@ -29,8 +29,8 @@ constexpr int kNarrow = 8;   // largest split count handled one wave per row
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
-                                                          const int32_t* __restrict__ num_splits, int B,
-                                                          int Hq, int max_splits, void* __restrict__ o,
+                                                          const int32_t* __restrict__ num_splits, int Hq,
+                                                          int max_splits, void* __restrict__ o,
                                                           float* __restrict__ lse) {
   constexpr int PER = D / 64;   // output elements per lane
   __shared__ float red[kWaves];
@@ -174,7 +174,7 @@ hipError_t launch_combine_lse(const CombineArgs& a, hipStream_t stream) {
   }
   const dim3 g((unsigned)rows);
 #define SA_LAUNCH(DD, BF)                                                                                   \
-  hipLaunchKernelGGL((combine_lse_kernel<DD, BF>), g, blk, 0, stream, a.part_o, a.part_lse, a.num_splits, a.B, \
+  hipLaunchKernelGGL((combine_lse_kernel<DD, BF>), g, blk, 0, stream, a.part_o, a.part_lse, a.num_splits,      \
                      a.Hq, a.max_splits, a.o, a.lse)
   if (a.d == 128) {
     if (a.out_bf16) SA_LAUNCH(128, true); else SA_LAUNCH(128, false);

@@ -146,7 +146,7 @@ __device__ void arrive_and_merge(unsigned char* smem, int32_t* counters, const f
 template <int D, bool FUSED, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void decode_splitkv_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ num_splits, int B, int Hq,
+    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ num_splits, int Hq,
     int Hkv, int S_cap, int max_splits, float c, float* __restrict__ part_o,
     float* __restrict__ part_lse, int32_t* __restrict__ counters, bf16* __restrict__ o,
     float* __restrict__ lse) {
@@ -418,7 +418,7 @@ hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t stream) {
   const bool fused = a.counters != nullptr;
 #define SA_LAUNCH(DD, FF)                                                                                   \
   hipLaunchKernelGGL((decode_splitkv_bf16_kernel<DD, FF, kWaves>), g, blk, 0, stream, (const bf16*)a.q,    \
-                     (const bf16*)a.k, (const bf16*)a.v, a.kv_len, a.num_splits, a.B, a.Hq, a.Hkv, a.S_cap, \
+                     (const bf16*)a.k, (const bf16*)a.v, a.kv_len, a.num_splits, a.Hq, a.Hkv, a.S_cap,      \
                      a.max_splits, c, a.part_o, a.part_lse, a.counters, (bf16*)a.o, a.lse)
   if (a.d == 128) {
     if (fused) SA_LAUNCH(128, true); else SA_LAUNCH(128, false);
