@@ -14,22 +14,24 @@ region):
   (``is_causal``, or an ``attn_mask`` that is causal).  A mask is
   ``masked_fill(M, -inf)``, an added bias of 0 / -inf, or SDPA's boolean
   (keep) or float (bias) ``attn_mask``, computed from constants, module
-  buffers and shapes only; its values are evaluated once at rewrite time and accepted when
-  they are exactly a causal mask ("AI Compiler pipeline stages", Pattern
-  Matching: ``MatMul(Q, K^T) -> Mask(causal) -> Softmax``), aligned top-left
-  (query t sees keys 0..t) or bottom-right (query t sees keys 0..Skv-Sq+t).
-  Between the softmax and the P V product, casts, ``contiguous`` and dropout
-  that is off (p = 0, or not training at rewrite time) are passed over.  K and
-  V repeated along the head dim for grouped-query attention
+  buffers and shapes only.  Its values are evaluated once at rewrite time
+  and accepted when they are exactly a causal mask ("AI Compiler pipeline
+  stages", Pattern Matching: ``MatMul(Q, K^T) -> Mask(causal) -> Softmax``),
+  aligned top-left (query t sees keys 0..t) or bottom-right (query t sees
+  keys 0..Skv-Sq+t).  Between the softmax and the P V product, casts,
+  ``contiguous`` and dropout that is off (p = 0, or not training at rewrite
+  time: the rewritten graph is for inference) are passed over.  K and V
+  repeated along the head dim for grouped-query attention
   (``repeat_interleave(G, dim=1)``, or the unsqueeze-expand-reshape idiom)
-  are matched back to the unrepeated tensors, which the kernel reads once per
-  KV head;
+  are matched back to the unrepeated tensors, which the kernel reads once
+  per KV head;
 * legality, from shapes and dtypes propagated on meta tensors: 4-D
   ``[B, H, S, d]`` operands of one dtype (bf16 or fp32), d 64 or 128, query
-  heads a multiple of KV heads (broadcast or ``enable_gqa``), and for causal
-  attention at most as many queries as keys;
-* rewrite: the matched nodes are replaced by one call of :func:`fused_attention`,
-  which runs ``attn_prefill`` (or split-KV + merge) through the binding.
+  heads a multiple of KV heads (one KV head, ``enable_gqa``, or repeated
+  K / V), and for causal attention at most as many queries as keys;
+* rewrite: the matched nodes are replaced by one call of
+  :func:`fused_attention`, which runs ``attn_prefill`` (or split-KV +
+  merge) through the binding.
 
 Graph edits only: nothing here computes attention.  Unmatched or illegal
 subgraphs are left as they are, and the report says why.
