@@ -151,3 +151,20 @@ def test_out_of_range_table_entries_and_lengths_are_clamped():
     table_eff = table.clamp(0, num_pages - 1)
     lens_eff = lens.clamp(max=3 * 64)
     _check(o, lse, q, kp, vp, table_eff, lens_eff, scale, range(B))
+
+
+def test_sequences_sharing_prefix_pages():
+    """Two sequences whose block tables point at the same first pages (a shared
+    prompt prefix), and one page listed twice in one table: pages are only
+    read, so any aliasing is allowed."""
+    B, Hq, Hkv, T_q, d, num_pages = 3, 16, 2, 3, 128, 7
+    g = torch.Generator(device=DEV).manual_seed(4444)
+    q = torch.randn((B, Hq, T_q, d), generator=g, device=DEV).to(torch.bfloat16)
+    kp = torch.randn((num_pages, Hkv, 64, d), generator=g, device=DEV).to(torch.bfloat16)
+    vp = torch.randn((num_pages, Hkv, 64, d), generator=g, device=DEV).to(torch.bfloat16)
+    table = torch.tensor([[5, 2, 0, 0], [5, 2, 6, 1], [3, 3, 4, 0]], dtype=torch.int32)
+    lens = torch.tensor([150, 250, 200], dtype=torch.int32)
+    scale = 1 / math.sqrt(d)
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), num_splits=2, scale=scale)
+    torch.cuda.synchronize()
+    _check(o, lse, q, kp, vp, table, lens, scale, range(B))
