@@ -474,6 +474,7 @@ def rewrite(module: torch.nn.Module, *example_inputs) -> tuple[fx.GraphModule, R
     for n in gm.graph.nodes:
         n.meta.update(by_name[n.name].meta)
     rep = Report([], [])
+    replaced = {}            # output node of a rewritten region -> its fused call
     for m in find_attention(gm):
         why = legality(m)
         if why is not None:
@@ -483,9 +484,13 @@ def rewrite(module: torch.nn.Module, *example_inputs) -> tuple[fx.GraphModule, R
         kw = {"causal": m.causal, "scale": scale}
         if m.causal and m.align != "top_left":
             kw["align"] = m.align
+        # an input may be the output of a region rewritten just before (the
+        # matches were all found on the original graph)
+        q, k, v = (replaced.get(x, x) for x in (m.q, m.k, m.v))
         with gm.graph.inserting_after(m.out):
-            fused = gm.graph.call_function(fused_attention, (m.q, m.k, m.v), kw)
+            fused = gm.graph.call_function(fused_attention, (q, k, v), kw)
         m.out.replace_all_uses_with(fused)
+        replaced[m.out] = fused
         rep.rewritten.append((m.out.name, m.kind, m.causal, scale))
     gm.graph.eliminate_dead_code()
     gm.recompile()

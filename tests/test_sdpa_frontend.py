@@ -254,6 +254,23 @@ def test_other_sdpa_masks_are_left_alone(mod, extra, why):
     assert len(rep.skipped) == 1 and why in rep.skipped[0][1], rep.skipped
 
 
+class TwoBlocks(torch.nn.Module):
+    """Two attention blocks in one graph: a causal SDPA call feeding an explicit chain."""
+
+    def forward(self, q, k, v):
+        h = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        return torch.softmax(h @ k.transpose(-2, -1) * 0.125, dim=-1) @ v + h
+
+
+def test_every_match_in_a_graph_is_rewritten():
+    q = _t(1, 2, 64, 64)
+    gm, rep = fe.rewrite(TwoBlocks(), q, q, q)
+    calls = _calls(gm)
+    assert len(calls) == 2 and len(rep.rewritten) == 2
+    assert sorted(c.kwargs["causal"] for c in calls) == [False, True]
+    assert calls[1].args[0] is calls[0] or calls[0].args[0] is calls[1]     # the second block reads the first
+
+
 def test_one_broadcast_kv_head_is_legal():
     gm, rep = fe.rewrite(Explicit(), _t(1, 8, 32, 64), _t(1, 1, 32, 64), _t(1, 1, 32, 64))
     assert len(_calls(gm)) == 1 and not rep.skipped
@@ -318,8 +335,12 @@ def _gpu_inputs(seed, shapes, dtype):
 
 
 def _run_rewritten(mod, args):
+    return _run_rewritten_n(mod, args, 1)
+
+
+def _run_rewritten_n(mod, args, n_calls):
     gm, rep = fe.rewrite(mod, *args)
-    assert len(_calls(gm)) == 1 and not rep.skipped
+    assert len(_calls(gm)) == n_calls and not rep.skipped
     left = {getattr(n.target, "__name__", str(n.target)) for n in gm.graph.nodes if n.op != "placeholder"}
     assert not left & {"matmul", "bmm", "softmax", "scaled_dot_product_attention"}, left
     out = gm(*args)
@@ -373,6 +394,19 @@ def test_rewritten_llama_style_gqa_matches_oracle(causal):
     o = _run_rewritten(mod, [q, k, v])
     O_ref, _ = oracle.attention(f64(q), f64(k), f64(v), 128 ** -0.5, causal)
     assert_o(o, O_ref.transpose(0, 2, 1, 3), "bf16")
+
+
+@pytest.mark.gpu
+def test_rewritten_two_block_graph_matches_oracle():
+    import oracle
+    from parity import assert_o, f64
+
+    q, k, v = _gpu_inputs(16, [(1, 4, 96, 64)] * 3, torch.bfloat16)
+    out = _run_rewritten_n(TwoBlocks(), [q, k, v], 2)
+    H, _ = oracle.attention(f64(q), f64(k), f64(v), 0.125, True)
+    h = torch.tensor(H, dtype=torch.float32).to(torch.bfloat16)       # the first block's output as the kernel stores it
+    O2, _ = oracle.attention(f64(h), f64(k), f64(v), 0.125, False)
+    assert_o(out, O2 + f64(h), "bf16")
 
 
 @pytest.mark.gpu
