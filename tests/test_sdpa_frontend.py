@@ -271,6 +271,36 @@ def test_every_match_in_a_graph_is_rewritten():
     assert calls[1].args[0] is calls[0] or calls[0].args[0] is calls[1]     # the second block reads the first
 
 
+class WeightsReturned(torch.nn.Module):
+    """The attention weights are an output too: the chain must stay as written."""
+
+    def forward(self, q, k, v):
+        w = torch.softmax(q @ k.transpose(-2, -1) * 0.125, dim=-1)
+        return w @ v, w
+
+
+class ScaledQShared(torch.nn.Module):
+    """Q is scaled once and the scaled Q is also used elsewhere."""
+
+    def forward(self, q, k, v):
+        qs = q * 0.125
+        return torch.softmax(qs @ k.transpose(-2, -1), dim=-1) @ v, qs.sum()
+
+
+def test_weights_used_elsewhere_keep_the_chain():
+    q = _t(1, 2, 32, 64)
+    gm, rep = fe.rewrite(WeightsReturned(), q, q, q)
+    assert not _calls(gm) and not rep.rewritten
+
+
+def test_a_scaled_q_with_other_users_stays_for_them():
+    q = _t(1, 2, 32, 64)
+    gm, rep = fe.rewrite(ScaledQShared(), q, q, q)
+    (call,) = _calls(gm)
+    assert call.args[0].name == "q" and call.kwargs["scale"] == 0.125
+    assert any(n.op == "call_method" and n.target == "sum" for n in gm.graph.nodes)
+
+
 def test_one_broadcast_kv_head_is_legal():
     gm, rep = fe.rewrite(Explicit(), _t(1, 8, 32, 64), _t(1, 1, 32, 64), _t(1, 1, 32, 64))
     assert len(_calls(gm)) == 1 and not rep.skipped
