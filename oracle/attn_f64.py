@@ -26,7 +26,6 @@ problem, not GPU implementation details):
 
 from __future__ import annotations
 
-import math
 
 import numpy as np
 
@@ -40,8 +39,8 @@ def visible_keys(Sq: int, Skv: int, causal: bool, kv_len: int | None = None,
                  rows=None) -> np.ndarray:
     """Boolean ``[n_rows, Skv]`` visibility of key ``j`` to query row ``t``.
 
-    Causal pattern: "AI Compiler pipeline stages", Pattern Matching
-    (``MatMul(Q, K^T) -> Mask(causal) -> Softmax``); alignment per ADR-0060
+    Causal pattern: "AI Compiler pipeline stages", Pattern Matching (a causal
+    mask between the score product and the softmax); alignment per ADR-0060
     section 0.5.3 / 5.4 (bottom-right, diagonal included).  ``kv_len`` per
     ADR-0060 section 5.2 (ragged last tile).
     """
@@ -316,11 +315,3 @@ def paged_attention(q, k_pages, v_pages, block_table, kv_len, scale: float):
         O[b], L[b] = attention(q[b:b + 1], kb[None], vb[None], scale, True)
     return O, L
 
-
-def lse_of_scores(scores) -> float:
-    """``ln sum exp`` of a 1-D score list, the plain way (test helper)."""
-    s = [float(x) for x in scores]
-    if not s:
-        return -math.inf
-    mx = max(s)
-    return mx + math.log(math.fsum(math.exp(x - mx) for x in s))
