@@ -30,9 +30,9 @@
  *    state between calls and is reentrant.
  *  - Tensors are dense and contiguous, row-major, in the shapes given below
  *    (last index fastest).  Every tensor pointer must be 16-byte aligned.
- *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
- *    All work is enqueued asynchronously on it; buffers must stay alive until
- *    the stream has passed the kernels.
+ *  - `stream` is a hipStream_t; NULL means the default stream.  All work is
+ *    enqueued asynchronously on it; buffers must stay alive until the stream
+ *    has passed the kernels.
  *  - Return value: ATTN_OK, or an error code.  On any error nothing has been
  *    enqueued and no output has been written.  Argument errors are detected on
  *    the host before any HIP call.  A failed kernel launch returns
@@ -40,6 +40,10 @@
  *  - Query head h reads KV head h / G with G = Hq / Hkv: the G query heads of
  *    one KV head are consecutive (ADR-0060 section 0, "CUBE Group").
  *  - Exponentials and logarithms are natural in every output; LSE = m + ln l.
+ *  - Element types: attn_prefill takes bf16 or fp32; every other entry point
+ *    that reads Q, K and V takes bf16 only (the split-KV, decode and paged
+ *    kernels exist for the bf16 serving path) and returns
+ *    ATTN_ERR_UNSUPPORTED for fp32.
  *  - Accumulation is fp32.  With bf16 inputs the probabilities are rounded to
  *    bf16 (round to nearest even) before the P V product, and O is rounded to
  *    bf16 on output.  LSE and split partials are always fp32.
@@ -48,6 +52,8 @@
 #define STREAMING_ATTENTION_ATTN_H
 
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -104,7 +110,7 @@ enum {
  */
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                  int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d,
-                 int32_t dtype, int32_t causal, float scale, void* stream);
+                 attn_dtype_t dtype, int32_t causal, float scale, hipStream_t stream);
 
 /*
  * attn_prefill_splitkv -- attn_prefill with the key range cut into splits, for
@@ -139,7 +145,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
  */
 int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* part_o, float* part_lse,
                          int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d,
-                         int32_t num_splits, int32_t dtype, int32_t causal, float scale, void* stream);
+                         int32_t num_splits, attn_dtype_t dtype, int32_t causal, float scale, hipStream_t stream);
 
 /*
  * attn_decode_splitkv -- one query token per sequence against a KV cache,
@@ -181,8 +187,8 @@ int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* par
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* kv_len, const int32_t* num_splits,
                         int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
-                        int32_t max_splits, int32_t dtype, float scale,
-                        float* part_o, float* part_lse, void* stream);
+                        int32_t max_splits, attn_dtype_t dtype, float scale,
+                        float* part_o, float* part_lse, hipStream_t stream);
 
 /*
  * attn_decode -- split-KV decode and the log-sum-exp merge in one launch.
@@ -209,9 +215,9 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* kv_len, const int32_t* num_splits,
                 int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
-                int32_t max_splits, int32_t dtype, float scale,
+                int32_t max_splits, attn_dtype_t dtype, float scale,
                 float* part_o, float* part_lse, int32_t* counters,
-                void* o, float* lse, void* stream);
+                void* o, float* lse, hipStream_t stream);
 
 /*
  * attn_decode_paged -- multi-token decode over a paged KV cache: every
@@ -262,8 +268,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                       const int32_t* kv_len, const int32_t* num_splits_seq, int32_t B, int32_t Hq, int32_t Hkv,
                       int32_t T_q, int32_t num_pages, int32_t max_pages, int32_t d, int32_t num_splits,
-                      int32_t dtype, float scale, float* part_o, float* part_lse, void* o, float* lse,
-                      void* stream);
+                      attn_dtype_t dtype, float scale, float* part_o, float* part_lse, void* o, float* lse,
+                      hipStream_t stream);
 
 /*
  * attn_combine_lse -- merge split partials into the final decode output.
@@ -288,7 +294,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
  */
 int attn_combine_lse(const float* part_o, const float* part_lse, const int32_t* num_splits,
                      int32_t B, int32_t Hq, int32_t max_splits, int32_t d,
-                     void* o, float* lse, int32_t out_dtype, void* stream);
+                     void* o, float* lse, attn_dtype_t out_dtype, hipStream_t stream);
 
 /* Short English text for a status code (static storage). */
 const char* attn_status_string(int status);

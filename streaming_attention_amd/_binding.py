@@ -78,13 +78,15 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _need(t, name, ndim, dtype=None, device=None):
+def _need(t, name, ndim, dtype=None, device=None, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -249,15 +251,15 @@ def combine_lse(part_o, part_lse, num_splits=None, out_dtype=torch.bfloat16, out
     if tuple(part_lse.shape) != (B, Hq, max_splits):
         raise ValueError("part_lse must be [B,Hq,max_splits]")
     if num_splits is not None:
-        _need(num_splits, "num_splits", 1, torch.int32, part_o.device)
+        _need(num_splits, "num_splits", 1, torch.int32, part_o.device, (B,))
     if out_dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported out_dtype {out_dtype}")
     if out is None:
         out = torch.empty((B, Hq, 1, d), dtype=out_dtype, device=part_o.device)
-    _need(out, "out", 4, out_dtype, part_o.device)
+    _need(out, "out", 4, out_dtype, part_o.device, (B, Hq, 1, d))
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=part_o.device)
-    _need(lse, "lse", 2, torch.float32, part_o.device)
+    _need(lse, "lse", 2, torch.float32, part_o.device, (B, Hq))
     st = lib().attn_combine_lse(_ptr(part_o), _ptr(part_lse), _ptr(num_splits), B, Hq, max_splits, d,
                                 _ptr(out), _ptr(lse), _DTYPE_CODE[out_dtype], _stream(part_o))
     _check(st, "attn_combine_lse")
@@ -325,10 +327,10 @@ def decode(q, k_cache, v_cache, kv_len=None, num_splits=None, max_splits: int = 
         raise ValueError("counters must hold B * Hkv entries")
     if out is None:
         out = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=q.device)
-    _need(out, "out", 4, torch.bfloat16, q.device)
+    _need(out, "out", 4, torch.bfloat16, q.device, (B, Hq, 1, d))
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _need(lse, "lse", 2, torch.float32, q.device)
+    _need(lse, "lse", 2, torch.float32, q.device, (B, Hq))
     st = lib().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(num_splits),
                            B, Hq, Hkv, S_cap, d, int(max_splits), ATTN_DTYPE_BF16, float(scale),
                            _ptr(part_o), _ptr(part_lse), _ptr(counters), _ptr(out), _ptr(lse), _stream(q))
@@ -391,10 +393,10 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_len, num_splits: int | Non
         n = int(num_splits)
     if out is None:
         out = torch.empty((B, Hq, T_q, d), dtype=torch.bfloat16, device=q.device)
-    _need(out, "out", 4, torch.bfloat16, q.device)
+    _need(out, "out", 4, torch.bfloat16, q.device, (B, Hq, T_q, d))
     if lse is None:
         lse = torch.empty((B, Hq, T_q), dtype=torch.float32, device=q.device)
-    _need(lse, "lse", 3, torch.float32, q.device)
+    _need(lse, "lse", 3, torch.float32, q.device, (B, Hq, T_q))
     po = pl = None
     if n > 1:
         po = torch.empty((B, Hq, T_q, n, d), dtype=torch.float32, device=q.device)

@@ -18,7 +18,7 @@ inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 // inside one (batch, KV head) slice are 32-bit on the GPU, so each such slice
 // of Q, K and V must stay under 2 GiB.
 int check_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq,
-                  int32_t Skv, int32_t d, int32_t dtype, int32_t causal, float scale, long long n_splits) {
+                  int32_t Skv, int32_t d, attn_dtype_t dtype, int32_t causal, float scale, long long n_splits) {
   if (B < 0 || Sq < 0 || Skv < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
   if (!good_scale(scale)) return ATTN_ERR_SHAPE;
@@ -54,8 +54,8 @@ const char* attn_status_string(int status) {
 }
 
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
-                 int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d, int32_t dtype, int32_t causal, float scale,
-                 void* stream) {
+                 int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d, attn_dtype_t dtype, int32_t causal, float scale,
+                 hipStream_t stream) {
   const int st = check_prefill(q, k, v, B, Hq, Hkv, Sq, Skv, d, dtype, causal, scale, 1);
   if (st != ATTN_OK || B == 0 || Sq == 0) return st;
   if (o == nullptr) return ATTN_ERR_NULL;
@@ -67,12 +67,12 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   a.bf16 = dtype == ATTN_DTYPE_BF16;
   a.causal = causal != 0;
   a.scale = scale;
-  return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return sa::launch_prefill(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* part_o, float* part_lse, int32_t B,
                          int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv, int32_t d, int32_t num_splits,
-                         int32_t dtype, int32_t causal, float scale, void* stream) {
+                         attn_dtype_t dtype, int32_t causal, float scale, hipStream_t stream) {
   if (num_splits < 1 || num_splits > 256) return ATTN_ERR_SHAPE;
   const int st = check_prefill(q, k, v, B, Hq, Hkv, Sq, Skv, d, dtype, causal, scale, num_splits);
   if (st != ATTN_OK) return st;
@@ -88,14 +88,14 @@ int attn_prefill_splitkv(const void* q, const void* k, const void* v, float* par
   a.causal = causal != 0;
   a.scale = scale;
   a.n_splits = num_splits; a.part_o = part_o; a.part_lse = part_lse;
-  return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return sa::launch_prefill(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                       const int32_t* kv_len, const int32_t* num_splits_seq, int32_t B, int32_t Hq, int32_t Hkv,
                       int32_t T_q, int32_t num_pages, int32_t max_pages, int32_t d, int32_t num_splits,
-                      int32_t dtype, float scale, float* part_o, float* part_lse, void* o, float* lse,
-                      void* stream) {
+                      attn_dtype_t dtype, float scale, float* part_o, float* part_lse, void* o, float* lse,
+                      hipStream_t stream) {
   if (B < 0 || T_q < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_pages < 1 || max_pages < 1)
     return ATTN_ERR_SHAPE;
   if (num_splits < 1 || num_splits > 256) return ATTN_ERR_SHAPE;
@@ -127,13 +127,13 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
   a.part_lse = num_splits > 1 ? part_lse : nullptr;
   a.block_table = block_table; a.kv_len = kv_len; a.max_pages = max_pages; a.num_pages = num_pages;
   a.seq_splits = num_splits > 1 ? num_splits_seq : nullptr;
-  return sa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return sa::launch_prefill(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
                         const int32_t* num_splits, int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
-                        int32_t max_splits, int32_t dtype, float scale, float* part_o, float* part_lse,
-                        void* stream) {
+                        int32_t max_splits, attn_dtype_t dtype, float scale, float* part_o, float* part_lse,
+                        hipStream_t stream) {
   if (B < 0 || S_cap < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
   if (!good_scale(scale)) return ATTN_ERR_SHAPE;
@@ -153,14 +153,14 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_cap = S_cap; a.d = d; a.max_splits = max_splits;
   a.scale = scale; a.part_o = part_o; a.part_lse = part_lse;
   a.counters = nullptr; a.o = nullptr; a.lse = nullptr;
-  return sa::launch_decode_splitkv(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+  return sa::launch_decode_splitkv(a, stream) == hipSuccess ? ATTN_OK
                                                                                             : ATTN_ERR_LAUNCH;
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
                 const int32_t* num_splits, int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
-                int32_t max_splits, int32_t dtype, float scale, float* part_o, float* part_lse, int32_t* counters,
-                void* o, float* lse, void* stream) {
+                int32_t max_splits, attn_dtype_t dtype, float scale, float* part_o, float* part_lse, int32_t* counters,
+                void* o, float* lse, hipStream_t stream) {
   if (B < 0 || S_cap < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
   if (!good_scale(scale)) return ATTN_ERR_SHAPE;
@@ -181,13 +181,13 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_cap = S_cap; a.d = d; a.max_splits = max_splits;
   a.scale = scale; a.part_o = part_o; a.part_lse = part_lse;
   a.counters = counters; a.o = o; a.lse = lse;
-  return sa::launch_decode_splitkv(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+  return sa::launch_decode_splitkv(a, stream) == hipSuccess ? ATTN_OK
                                                                                             : ATTN_ERR_LAUNCH;
 }
 
 int attn_combine_lse(const float* part_o, const float* part_lse, const int32_t* num_splits, int32_t B,
-                     int32_t Hq, int32_t max_splits, int32_t d, void* o, float* lse, int32_t out_dtype,
-                     void* stream) {
+                     int32_t Hq, int32_t max_splits, int32_t d, void* o, float* lse, attn_dtype_t out_dtype,
+                     hipStream_t stream) {
   if (B < 0 || Hq < 1) return ATTN_ERR_SHAPE;
   if (max_splits < 1 || max_splits > 256) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
@@ -201,7 +201,7 @@ int attn_combine_lse(const float* part_o, const float* part_lse, const int32_t* 
   a.part_o = part_o; a.part_lse = part_lse; a.num_splits = num_splits;
   a.B = B; a.Hq = Hq; a.max_splits = max_splits; a.d = d;
   a.o = o; a.lse = lse; a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
-  return sa::launch_combine_lse(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK
+  return sa::launch_combine_lse(a, stream) == hipSuccess ? ATTN_OK
                                                                                         : ATTN_ERR_LAUNCH;
 }
 

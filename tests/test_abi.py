@@ -26,7 +26,7 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_every_entry_point():
     names = declared_functions()
     for n in ("attn_prefill", "attn_prefill_splitkv", "attn_decode_splitkv", "attn_combine_lse", "attn_decode",
               "attn_decode_paged", "attn_status_string"):
@@ -187,3 +187,37 @@ def test_splits_for_lengths():
     n = sa.splits_for_lengths(torch.tensor([0, 1, 2048, 2049, 131072, 10 ** 7]))
     assert n.tolist() == [1, 1, 1, 2, 64, 64]
     assert n.dtype == torch.int32
+
+
+@pytest.mark.gpu
+def test_binding_rejects_output_buffers_of_the_wrong_shape():
+    """Caller-supplied outputs and split counts are checked against the shapes
+    the kernels write before anything is launched."""
+    dev = "cuda"
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    B, Hq, Hkv, S, d, n = 2, 8, 2, 128, 128, 4
+    q = torch.zeros(B, Hq, 1, d, device=dev, dtype=bf)
+    kc = torch.zeros(B, Hkv, S, d, device=dev, dtype=bf)
+    po = torch.zeros(B, Hq, n, d, device=dev, dtype=f32)
+    pl = torch.zeros(B, Hq, n, device=dev, dtype=f32)
+    with pytest.raises(ValueError, match="shape"):
+        sa.combine_lse(po, pl, torch.ones(B + 1, device=dev, dtype=i32))
+    with pytest.raises(ValueError, match="shape"):
+        sa.combine_lse(po, pl, None, bf, out=torch.zeros(B, Hq - 1, 1, d, device=dev, dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        sa.combine_lse(po, pl, None, bf, lse=torch.zeros(B, 1, device=dev, dtype=f32))
+    with pytest.raises(ValueError, match="shape"):
+        sa.decode(q, kc, kc, max_splits=n, fused=True, out=torch.zeros(1, Hq, 1, d, device=dev, dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        sa.decode(q, kc, kc, max_splits=n, fused=True, lse=torch.zeros(B, Hq - 1, device=dev, dtype=f32))
+    with pytest.raises(ValueError, match="shape"):
+        sa.decode(q, kc, kc, max_splits=n, out=torch.zeros(B, Hq, 2, d, device=dev, dtype=bf))
+    T_q = 4
+    qp = torch.zeros(B, Hq, T_q, d, device=dev, dtype=bf)
+    pool = torch.zeros(6, Hkv, 64, d, device=dev, dtype=bf)
+    table = torch.zeros(B, 3, device=dev, dtype=i32)
+    lens = torch.full((B,), 100, device=dev, dtype=i32)
+    with pytest.raises(ValueError, match="shape"):
+        sa.decode_paged(qp, pool, pool, table, lens, 1, out=torch.zeros(B, Hq, 1, d, device=dev, dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        sa.decode_paged(qp, pool, pool, table, lens, 1, lse=torch.zeros(B, Hq, 1, device=dev, dtype=f32))
