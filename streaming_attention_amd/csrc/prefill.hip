@@ -547,12 +547,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += psum[qb];
   };
 
-  // Software pipeline (the pages' "issue the next Q K^T before this tile's
-  // softmax", one stage deeper): iteration kt (parity P = kt % 2) loads K tile
-  // kt + 2 into K slot P and V tile kt into V slot P -- slots iteration kt - 1
-  // finished reading -- while it computes the scores of tile kt + 1 from K
-  // slot 1 - P, the softmax of tile kt, and the P V product of tile kt - 1 from
-  // V slot 1 - P.  One barrier per tile, after this wave's loads have landed,
+  // Software pipeline (ADR-0060 section 5.6, option 3: the next tile's score
+  // GEMM is started before this tile's softmax; here one stage deeper):
+  // iteration kt (parity P = kt % 2) loads K tile kt + 2 into K slot P and V
+  // tile kt into V slot P -- slots iteration kt - 1 finished reading -- while
+  // it computes the scores of tile kt + 1 from K slot 1 - P, the softmax of
+  // tile kt, and the P V product of tile kt - 1 from V slot 1 - P.  One barrier per tile, after this wave's loads have landed,
   // orders the rings.  The P V product of the last tile follows the loop.
   kt_lo = __builtin_amdgcn_readfirstlane(kt_lo);
   kt_hi = __builtin_amdgcn_readfirstlane(kt_hi);

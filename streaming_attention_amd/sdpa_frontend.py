@@ -1,11 +1,11 @@
 """SDPA-pattern front end: find scaled-dot-product attention in a torch.fx
 graph and route it to the library's fused kernel.
 
-The three steps follow "AI Compiler pipeline stages" (Pattern Matching ->
-Legality Checking -> Rewrite) and "MCIR Minimal Implementation Design"
-section 9 (the attention pattern MatMul(Q, K^T) -> Mask? -> Softmax ->
-MatMul(., V) found in the operator graph, then lowered to a streaming
-region):
+The three steps follow "AI Compiler pipeline stages" (its pattern matching,
+legality checking and rewrite stages) and "MCIR Minimal Implementation
+Design" section 9 (the score product, an optional mask, the softmax and the
+product with V are recognised as one attention pattern in the operator graph
+and lowered to a streaming region):
 
 * pattern: ``softmax(mask(scale * (Q @ K^T)), dim=-1) @ V`` written out (the
   scale as a constant multiply or divide of the scores, or of Q, before or
@@ -15,10 +15,13 @@ region):
   ``masked_fill(M, -inf)``, an added bias of 0 / -inf, or SDPA's boolean
   (keep) or float (bias) ``attn_mask``, computed from constants, module
   buffers and shapes only.  Its values are evaluated once at rewrite time
-  and accepted when they are exactly a causal mask ("AI Compiler pipeline
-  stages", Pattern Matching: ``MatMul(Q, K^T) -> Mask(causal) -> Softmax``),
-  aligned top-left (query t sees keys 0..t) or bottom-right (query t sees
-  keys 0..Skv-Sq+t).  Between the softmax and the P V product, casts,
+  and accepted when they are exactly a causal mask (the causal attention
+  pattern of "AI Compiler pipeline stages", Pattern Matching), aligned
+  top-left (query t sees keys 0..t) or bottom-right (query t sees keys
+  0..Skv-Sq+t); the rewritten call then refuses other lengths, since a
+  window or padding mask can look causal at one length only.  Flags of an
+  SDPA call computed from shapes (``is_causal=q.shape[2] > 1``) count as
+  constants; flags that depend on data leave the call alone.  Between the softmax and the P V product, casts,
   ``contiguous`` and dropout that is off (p = 0, or not training at rewrite
   time: the rewritten graph is for inference) are passed over.  K and V
   repeated along the head dim for grouped-query attention
@@ -55,14 +58,21 @@ _MATMUL = {torch.matmul, operator.matmul}
 _SDPA = torch.nn.functional.scaled_dot_product_attention
 
 
-def fused_attention(q, k, v, causal: bool, scale: float, align: str = "top_left"):
+def fused_attention(q, k, v, causal: bool, scale: float, align: str = "top_left", lengths=None):
     """The rewritten region: softmax(scale Q K^T [+ causal mask]) V on the GPU.
 
     SDPA's ``is_causal`` mask is top-left aligned (query t sees keys 0..t); the
     kernel aligns bottom-right (the last query sees every key), so with fewer
     queries than keys a top-left mask passes only the first Sq keys -- the only
     ones any query can see.
+
+    ``lengths = (Sq, Skv)``: the region's mask was recognised from its values
+    at these lengths only (a window or padding mask can look causal at one
+    length and not at another), so other lengths are refused.
     """
+    if lengths is not None and (q.shape[2], k.shape[2]) != tuple(lengths):
+        raise ValueError(f"this attention region's mask was checked at (Sq, Skv) = {tuple(lengths)}; "
+                         f"called with {(q.shape[2], k.shape[2])}: rewrite the module at these lengths")
     if causal and align == "top_left" and q.shape[2] < k.shape[2]:
         k = k[:, :, :q.shape[2]]
         v = v[:, :, :q.shape[2]]
@@ -81,7 +91,8 @@ class Match:
     kind: str                # "explicit" or "sdpa"
     gqa: bool = False        # SDPA's enable_gqa, or K / V repeats matched away
     align: str = "top_left"  # causal mask alignment: "top_left" or "bottom_right"
-    mask_error: str | None = None   # why a mask in the chain is not a causal mask
+    error: str | None = None        # why the region cannot be rewritten (its mask, a non-constant argument)
+    mask_lengths: tuple | None = None   # (Sq, Skv) at which a mask's values were checked
 
 
 def _const(x):
@@ -90,6 +101,18 @@ def _const(x):
     if isinstance(x, fx.Node):
         x = x.meta.get("scalar_value")
     return x if isinstance(x, (int, float)) and not isinstance(x, bool) else None
+
+
+_UNKNOWN = object()
+
+
+def _static(x):
+    """The value x stands for: a literal, or a node whose value shape
+    propagation found to depend on shapes only (numbers, bools, sizes);
+    ``_UNKNOWN`` for a node whose value depends on an input's data."""
+    if isinstance(x, fx.Node):
+        return x.meta.get("static_value", _UNKNOWN)
+    return x
 
 
 def _is_static(x) -> bool:
@@ -106,6 +129,8 @@ class _ShapeAndScalarProp(ShapeProp):
 
     def run_node(self, n):
         result = super().run_node(n)
+        if n.op == "placeholder":                 # an input's value is the caller's, not a constant
+            return result
         if isinstance(result, torch.device):      # masks are evaluated on the CPU
             n.meta["static_value"] = torch.device("cpu")
         if _is_static(result):
@@ -355,11 +380,12 @@ def _explicit_mask(gm, m: Match, mask_node, how: str) -> None:
     its alignment; a non-causal mask leaves m illegal with the reason."""
     tq, tk = _meta(m.q), _meta(m.k)
     if tq is None or tk is None or len(tq.shape) < 2 or len(tk.shape) < 2:
-        m.mask_error = "no shape information for the mask"
+        m.error = "no shape information for the mask"
         return
     align, why = _mask_alignment(gm, mask_node, how, tq.shape[-2], tk.shape[-2])
     m.causal = why is None
-    m.align, m.mask_error = (align or "top_left"), why
+    m.align, m.error = (align or "top_left"), why
+    m.mask_lengths = (int(tq.shape[-2]), int(tk.shape[-2]))
 
 
 def find_attention(gm: fx.GraphModule) -> list[Match]:
@@ -369,12 +395,28 @@ def find_attention(gm: fx.GraphModule) -> list[Match]:
         if n.op == "call_function" and n.target is _SDPA:
             args = list(n.args) + [None] * (3 - len(n.args))
             kw = n.kwargs
-            if kw.get("dropout_p", n.args[4] if len(n.args) > 4 else 0.0) not in (0, 0.0):
+            # Flags may be graph values computed from shapes (is_causal=q.shape[2] > 1,
+            # scale=q.shape[-1] ** -0.5): their static values decide; a flag that
+            # depends on an input's data leaves the call as it is.
+            dropout = _static(kw.get("dropout_p", n.args[4] if len(n.args) > 4 else 0.0))
+            causal = _static(kw.get("is_causal", n.args[5] if len(n.args) > 5 else False))
+            scale = _static(kw.get("scale", n.args[6] if len(n.args) > 6 else None))
+            gqa = _static(kw.get("enable_gqa", False))
+            unknown = [name for name, val in (("dropout_p", dropout), ("is_causal", causal), ("scale", scale),
+                                              ("enable_gqa", gqa)) if val is _UNKNOWN]
+            if not unknown and dropout not in (0, 0.0):
                 continue
-            causal = bool(kw.get("is_causal", n.args[5] if len(n.args) > 5 else False))
-            scale = kw.get("scale", n.args[6] if len(n.args) > 6 else None)
-            gqa = bool(kw.get("enable_gqa", False))
-            m = Match(args[0], args[1], args[2], None if scale is None else float(scale), causal, n, "sdpa", gqa)
+            m = Match(args[0], args[1], args[2], None, False, n, "sdpa")
+            if unknown:
+                m.error = f"{', '.join(unknown)} not a constant at rewrite time"
+                found.append(m)
+                continue
+            if scale is not None and (not isinstance(scale, (int, float)) or isinstance(scale, bool)):
+                m.error = f"scale {scale!r} is not a number"
+                found.append(m)
+                continue
+            m.scale = None if scale is None else float(scale)
+            m.causal, m.gqa = bool(causal), bool(gqa)
             attn_mask = kw.get("attn_mask", n.args[3] if len(n.args) > 3 else None)
             if attn_mask is not None:   # (PyTorch allows no is_causal with it)
                 # SDPA's boolean mask keeps the True entries; a float mask is added to the scores.
@@ -430,8 +472,8 @@ def legality(m: Match) -> str | None:
     tq, tk, tv = _meta(m.q), _meta(m.k), _meta(m.v)
     if tq is None or tk is None or tv is None:
         return "no shape information"
-    if m.mask_error is not None:
-        return m.mask_error
+    if m.error is not None:
+        return m.error
     if len(tq.shape) != 4 or len(tk.shape) != 4 or len(tv.shape) != 4:
         return "operands are not [B, H, S, d]"
     if not (tq.dtype == tk.dtype == tv.dtype) or tq.dtype not in (torch.bfloat16, torch.float32):
@@ -484,6 +526,8 @@ def rewrite(module: torch.nn.Module, *example_inputs) -> tuple[fx.GraphModule, R
         kw = {"causal": m.causal, "scale": scale}
         if m.causal and m.align != "top_left":
             kw["align"] = m.align
+        if m.mask_lengths is not None:
+            kw["lengths"] = m.mask_lengths
         # an input may be the output of a region rewritten just before (the
         # matches were all found on the original graph)
         q, k, v = (replaced.get(x, x) for x in (m.q, m.k, m.v))

@@ -98,15 +98,15 @@ def test_causal_masks_in_the_chain_are_recognised():
     q = _t(1, 2, 100, 64)
     gm, rep = fe.rewrite(BufferCausal(), q, q, q)
     (call,) = _calls(gm)
-    assert call.kwargs == {"causal": True, "scale": pytest.approx(0.125)}
+    assert call.kwargs == {"causal": True, "scale": pytest.approx(0.125), "lengths": (100, 100)}
     assert not [n for n in gm.graph.nodes if n.op == "get_attr"]          # the mask buffer is no longer read
     kv = _t(1, 2, 300, 64)
     gm, rep = fe.rewrite(BottomRightCausal(), q, kv, kv)
     (call,) = _calls(gm)
-    assert call.kwargs == {"causal": True, "scale": 0.125, "align": "bottom_right"}
+    assert call.kwargs == {"causal": True, "scale": 0.125, "align": "bottom_right", "lengths": (100, 300)}
     gm, rep = fe.rewrite(AdditiveMask(_additive(100, 300, 1)), q, kv, kv)
     (call,) = _calls(gm)
-    assert call.kwargs == {"causal": True, "scale": 0.125}                   # top-left
+    assert call.kwargs == {"causal": True, "scale": 0.125, "lengths": (100, 300)}   # top-left
     gm, rep = fe.rewrite(AdditiveMask(_additive(100, 300, 201).view(1, 1, 100, 300)), q, kv, kv)
     (call,) = _calls(gm)
     assert call.kwargs["align"] == "bottom_right"
@@ -237,10 +237,10 @@ def test_sdpa_causal_attn_masks_are_recognised():
     keep = torch.ones(100, 300, dtype=torch.bool).tril()                      # top-left
     gm, rep = fe.rewrite(SdpaMask(keep), q, kv, kv)
     (call,) = _calls(gm)
-    assert call.kwargs == {"causal": True, "scale": pytest.approx(0.125)}
+    assert call.kwargs == {"causal": True, "scale": pytest.approx(0.125), "lengths": (100, 300)}
     gm, rep = fe.rewrite(SdpaMask(_additive(100, 300, 201), scale=0.5), q, kv, kv)   # bottom-right, float
     (call,) = _calls(gm)
-    assert call.kwargs == {"causal": True, "scale": 0.5, "align": "bottom_right"}
+    assert call.kwargs == {"causal": True, "scale": 0.5, "align": "bottom_right", "lengths": (100, 300)}
 
 
 @pytest.mark.parametrize("mod,extra,why", [
@@ -344,6 +344,71 @@ def test_illegal_matches_are_left_alone(mod, shapes, dtype, why):
     gm, rep = fe.rewrite(mod, *args)
     assert not _calls(gm)
     assert len(rep.skipped) == 1 and why in rep.skipped[0][1]
+
+
+class SdpaShapeFlags(torch.nn.Module):
+    """SDPA flags computed from shapes: causal only when there is more than
+    one query, the scale from the head dim."""
+
+    def forward(self, q, k, v):
+        return F.scaled_dot_product_attention(q, k, v, is_causal=q.shape[2] > 1, scale=q.shape[-1] ** -0.5)
+
+
+class SdpaFlagInput(torch.nn.Module):
+    """The causal flag is an input of the graph: its value at rewrite time says
+    nothing about later calls."""
+
+    def forward(self, q, k, v, causal):
+        return F.scaled_dot_product_attention(q, k, v, is_causal=causal)
+
+
+def test_sdpa_flags_computed_from_shapes_take_their_values():
+    """is_causal = (Sq > 1) is False for one query: the rewrite must not be
+    causal (a causal top-left call would see only key 0)."""
+    q, kv = _t(1, 2, 1, 64), _t(1, 2, 40, 64)
+    gm, rep = fe.rewrite(SdpaShapeFlags(), q, kv, kv)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": False, "scale": pytest.approx(0.125)}
+    q = _t(1, 2, 40, 128)
+    gm, rep = fe.rewrite(SdpaShapeFlags(), q, q, q)
+    (call,) = _calls(gm)
+    assert call.kwargs == {"causal": True, "scale": pytest.approx(1 / math.sqrt(128))}
+
+
+def test_sdpa_flags_that_are_inputs_are_left_alone():
+    q = _t(1, 2, 8, 64)
+    gm, rep = fe.rewrite(SdpaFlagInput(), q, q, q, True)
+    assert not _calls(gm)
+    assert len(rep.skipped) == 1 and "is_causal not a constant" in rep.skipped[0][1], rep.skipped
+
+
+class SlidingWindow(torch.nn.Module):
+    """A causal mask limited to the last `window` keys: causal-looking while
+    every sequence is shorter than the window."""
+
+    def __init__(self, window):
+        super().__init__()
+        self.window = window
+
+    def forward(self, q, k, v):
+        T = q.shape[2]
+        ones = q.new_ones(T, T, dtype=torch.bool)
+        hide = ones.triu(1) | ones.tril(-self.window)
+        s = (q @ k.transpose(-2, -1)).masked_fill(hide, float("-inf"))
+        return torch.softmax(s * 0.125, dim=-1) @ v
+
+
+def test_a_window_mask_is_only_trusted_at_the_lengths_it_was_checked():
+    q = _t(1, 2, 64, 64)
+    gm, rep = fe.rewrite(SlidingWindow(100), q, q, q)          # at T = 64 the window hides nothing
+    (call,) = _calls(gm)
+    assert call.kwargs["lengths"] == (64, 64)
+    big = _t(1, 2, 200, 64)
+    with pytest.raises(ValueError, match="checked at"):
+        gm(big, big, big)                                      # refused before anything runs
+    gm, rep = fe.rewrite(SlidingWindow(100), big, big, big)    # at T = 200 the window shows
+    assert not _calls(gm)
+    assert len(rep.skipped) == 1 and "not causal" in rep.skipped[0][1]
 
 
 def test_masked_or_dropout_sdpa_and_other_softmaxes_are_not_matched():
