@@ -10,11 +10,17 @@ One step = one pass of the whole path on resident synthetic inputs:
 Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s
 (4 * d * visible (q, k) pairs per head / prefill kernel time); the decode
 throughput in KV GB/s (every valid K and V byte once / split + combine time)
-is reported next to it.  Outside the step, the chunked prefill (512 queries
-after a 65536-token prefix, split-KV + merge) and the multi-token decode over a
-paged cache (16 sequences x 4 tokens, lengths 1K-32K) are timed on their own
-and reported as `chunked_prefill` and `paged_decode`.  Kernel times come from HIP events recorded on the
-stream the kernels run on, over the timed steps.  The float64 oracle, timed on
+is reported next to it.  Outside the step, after it, these are timed on their
+own and reported under their own keys:
+  * `ragged_decode`: split-KV decode of 16 sequences with lengths uniform in
+    [1024, 131072], split count per length, + merge;
+  * `chunked_prefill`: 512 queries after a 65536-token prefix, split-KV + merge;
+  * `mha_causal_prefill`: causal MHA prefill B=2, H=16, S=1024, d=64 (report
+    only: a launch-latency-sized problem);
+  * `paged_decode`: multi-token decode over a paged cache (16 sequences x 4
+    tokens, lengths 1K-32K).
+Kernel times come from HIP events recorded on the stream the kernels run on,
+over the timed steps.  The float64 oracle, timed on
 the host cores on a bounded sample of the same prefill workload, is reported as
 `cpu_baseline` (a baseline only).
 
@@ -58,6 +64,8 @@ TRAFFIC = {
                 "fetch_kib": 140591 + 16917, "write_kib": 33282 + 8448},
     "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "068b81e27a31b0cc",
               "fetch_kib": 592147 + 8278, "write_kib": 17410 + 1056},
+    "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": None,
+               "fetch_kib": None, "write_kib": None},
 }
 
 
@@ -78,7 +86,7 @@ def code_hash(sources):
 def measured_traffic(name):
     """HBM bytes per launch (fetch + write, copy-calibrated), or None if stale."""
     t = TRAFFIC[name]
-    if code_hash(t["sources"]) != t["sha256_16"]:
+    if t["sha256_16"] is None or code_hash(t["sources"]) != t["sha256_16"]:
         return None
     return int(t["fetch_kib"] * 1024 / FETCH_SCALE + t["write_kib"] * 1024 / WRITE_SCALE)
 
@@ -89,10 +97,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "chunked", "paged", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "chunked", "paged", "ragged", "mha", "copy"],
+                    default="all",
                     help="run only one part (for per-kernel profiling runs): one half of the step, the "
-                         "chunked prefill, the paged multi-token decode, or 'copy', a plain 1 GiB device copy "
-                         "that is the reference for scaling HBM byte counters")
+                         "chunked prefill, the paged multi-token decode, the ragged decode, the small MHA "
+                         "prefill, or 'copy', a plain 1 GiB device copy that is the reference for scaling "
+                         "HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -142,6 +152,71 @@ def cpu_baseline(target_s: float):
     }
 
 
+def timed_mean_ms(fn, warmup: int, steps: int, stream) -> float:
+    """Mean time of one call of fn over `steps` calls after `warmup` untimed
+    ones: HIP events recorded on the launch stream around the timed calls."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_ragged(sa, W, dev, stream, warmup, steps):
+    """Ragged decode: B=16, lengths uniform in [1024, 131072] from the seed,
+    splits per length (splits_for_lengths), split-KV + merge."""
+    import torch
+
+    wr = W.RAGGED_DECODE
+    qr, kr, vr, lens_r = W.decode_inputs(wr, dev)
+    ns = sa.splits_for_lengths(lens_r)
+    lens_d, ns_d = lens_r.to(dev), ns.to(dev)
+    po = torch.empty((wr.B, wr.Hq, 64, wr.d), dtype=torch.float32, device=dev)
+    pl = torch.empty((wr.B, wr.Hq, 64), dtype=torch.float32, device=dev)
+    o = torch.empty((wr.B, wr.Hq, 1, wr.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wr.B, wr.Hq), dtype=torch.float32, device=dev)
+
+    def call():
+        sa.decode(qr, kr, vr, lens_d, ns_d, max_splits=64, scale=wr.scale, part_o=po, part_lse=pl, out=o, lse=lse)
+
+    ms = timed_mean_ms(call, warmup, steps, stream)
+    kv = W.decode_kv_bytes(lens_r, wr.Hkv, wr.d)
+    gbs = kv / (ms * 1e-3) / 1e9
+    return {"workload": f"ragged split-KV decode B={wr.B} Hq={wr.Hq} Hkv={wr.Hkv} d={wr.d} bf16, lengths "
+                        f"U[{wr.len_lo},{wr.len_hi}] (seed {wr.seed}: sum {int(lens_r.sum())}), splits per "
+                        f"length min(64, ceil(len/2048)) (sum {int(ns.sum())})",
+            "kernels": "decode_splitkv_bf16_kernel<128> + combine_lse_kernel<128>",
+            "us": round(ms * 1e3, 2), "kv_gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "kv_bytes": kv,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("ragged"),
+                         "traffic_unit": "HBM bytes per call, split + merge (fetch + write)"}}
+
+
+def measure_mha(sa, W, dev, stream, warmup, steps):
+    """Causal MHA prefill B=2, H=16, S=1024, d=64 (bf16): report only."""
+    import torch
+
+    wm = W.MHA_CAUSAL
+    qm, km, vm = W.prefill_inputs(wm, dev)
+    om = torch.empty_like(qm)
+    lsem = torch.empty((wm.B, wm.Hq, wm.Sq), dtype=torch.float32, device=dev)
+    ms = timed_mean_ms(lambda: sa.prefill(qm, km, vm, causal=True, scale=wm.scale, out=om, lse=lsem),
+                       warmup, steps, stream)
+    tf = wm.flops() / (ms * 1e-3) / 1e12
+    return {"workload": f"causal MHA prefill B={wm.B} H={wm.Hq} S={wm.Sq} d={wm.d} bf16 (report only)",
+            "kernels": "prefill_bf16_kernel<64,causal>", "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+            "pct_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2),
+            "algorithmic_gflop": round(wm.flops() / 1e9, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -186,6 +261,8 @@ def main():
     do_dc = args.only in ("all", "decode")
     do_ch = args.only in ("all", "chunked")
     do_pg = args.only in ("all", "paged")
+    do_rg = args.only in ("all", "ragged")
+    do_mh = args.only in ("all", "mha")
 
     def step(i=None):
         if i is not None:
@@ -216,6 +293,15 @@ def main():
         pf_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)) / n_ev
         dc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)) / n_ev
     ms_step = wall * 1e3 / args.steps
+
+    ragged = None
+    if do_rg:   # ragged split-KV decode + merge, timed on its own (not part of the step)
+        ragged = measure_ragged(sa, W, dev, stream, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+
+    mha = None
+    if do_mh:
+        mha = measure_mha(sa, W, dev, stream, args.warmup, args.steps)
 
     chunked = None
     if do_ch:   # split-KV prefill + merge, timed on its own (not part of the step)
@@ -331,12 +417,15 @@ def main():
         },
         "device": torch.cuda.get_device_name(dev),
     }
+    if ragged is not None:
+        result["ragged_decode"] = ragged
     if chunked is not None:
         result["chunked_prefill"] = chunked
+    if mha is not None:
+        result["mha_causal_prefill"] = mha
     if paged is not None:
         result["paged_decode"] = paged
     if not args.no_cpu_baseline:
-        del q, k, v, o, lse, qd, kc, vc, part_o, part_lse, od, lsed
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -79,3 +79,57 @@ def prefill_split_bounds(Skv: int, n: int, tile: int = 64):
     T = -(-Skv // tile)
     c = -(-T // n) if T > 0 else 0
     return [(min(tile * s * c, Skv), min(tile * (s + 1) * c, Skv)) for s in range(n)]
+
+
+def block_rows(n_rows: int, rng, block: int = 128, per_block: int = 1):
+    """Rows to check in a long output: ``per_block`` random rows of every
+    ``block``-row block, plus the first and the last row."""
+    rows = {0, n_rows - 1} if n_rows else set()
+    for s in range(0, n_rows, block):
+        rows.update(int(x) for x in rng.integers(s, min(s + block, n_rows), per_block))
+    return sorted(rows)
+
+
+def check_prefill_rows(o, lse, q, k, v, scale, causal, rows, heads=None, block: int = 128, what: str = ""):
+    """The listed query rows of every (batch, query head) against the oracle:
+    max abs error of O and LSE at the bf16 bar, and the relative Frobenius
+    error of the checked rows of each ``block``-row block taken together.
+    Returns (worst O error, worst LSE error, worst relative error)."""
+    import oracle
+
+    B, Hq, Sq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = torch.as_tensor(rows, device=o.device)
+    heads = range(Hq) if heads is None else heads
+    worst = [0.0, 0.0, 0.0]
+    for b in range(B):
+        kv_cache = {}
+        for h in heads:
+            kvh = h // G
+            if kvh not in kv_cache:
+                kv_cache = {kvh: (f64(k[b:b + 1, kvh:kvh + 1]), f64(v[b:b + 1, kvh:kvh + 1]))}
+            kh, vh = kv_cache[kvh]
+            O_ref, L_ref = oracle.attention_rows(f64(q[b:b + 1, h:h + 1]), kh, vh, scale, causal, 0, 0, rows)
+            tag = f"{what} b{b} h{h}"
+            got = f64(o[b, h][idx])
+            worst[0] = max(worst[0], assert_o(got, O_ref, "bf16", "O" + tag))
+            worst[1] = max(worst[1], assert_lse(lse[b, h][idx], L_ref, "bf16", "LSE" + tag))
+            for blk in np.unique(rows // block):
+                sel = rows // block == blk
+                num = np.linalg.norm(got[sel] - O_ref[sel])
+                den = np.linalg.norm(O_ref[sel])
+                rel = num / den if den > 0 else num
+                assert rel <= REL_FRO_TOL, f"O{tag} rows {blk * block}..: relative Frobenius error {rel:.3e}"
+                worst[2] = max(worst[2], float(rel))
+    return tuple(worst)
+
+
+def nan_outputs(q, lse_shape=None):
+    """Output buffers filled with NaN, so that an output row the kernel never
+    writes stays NaN and is caught."""
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(tuple(q.shape[:3]) if lse_shape is None else lse_shape, float("nan"),
+                     dtype=torch.float32, device=q.device)
+    return o, lse
