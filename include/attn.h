@@ -72,7 +72,8 @@ enum {
   ATTN_ERR_SHAPE = 2,       /* a size, the scale or the causal/size relation is invalid */
   ATTN_ERR_UNSUPPORTED = 3, /* valid request the library does not implement     */
   ATTN_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned          */
-  ATTN_ERR_LAUNCH = 5       /* the HIP kernel launch failed                     */
+  ATTN_ERR_LAUNCH = 5,      /* the HIP kernel launch failed                     */
+  ATTN_ERR_WORKSPACE = 6    /* larger than attn_decode_noalloc's fixed workspace */
 };
 
 /*
@@ -218,6 +219,34 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 int32_t max_splits, attn_dtype_t dtype, float scale,
                 float* part_o, float* part_lse, int32_t* counters,
                 void* o, float* lse, hipStream_t stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode_splitkv followed by attn_combine_lse, with
+ * the split partials kept in a fixed workspace inside the library instead of
+ * caller buffers.  For callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It calls no allocating routine.
+ *
+ *   (q ... scale)   exactly as for attn_decode_splitkv (same split plan)
+ *   o          [B, Hq, 1, d] bf16 (written)
+ *   lse        [B, Hq] float32 (written); may be NULL
+ *
+ * Workspace: a device array of the library, (128 + 1) * 4 bytes per partial for
+ * ATTN_NOALLOC_MAX_PARTIALS partials (32.25 MiB), one copy per GPU, held
+ * until the process ends.  Requires B * Hq * max_splits <=
+ * ATTN_NOALLOC_MAX_PARTIALS, else ATTN_ERR_WORKSPACE.  Every call on one GPU
+ * uses the same array and leaves the last call's partials in it: calls that
+ * overlap in time on one GPU (on different streams) race; calls ordered on
+ * one stream do not.
+ * Errors: as attn_decode_splitkv, plus ATTN_ERR_NULL for o and
+ * ATTN_ERR_WORKSPACE.
+ */
+#define ATTN_NOALLOC_MAX_PARTIALS 65536
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* kv_len, const int32_t* num_splits,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t S_cap, int32_t d,
+                        int32_t max_splits, attn_dtype_t dtype, float scale,
+                        void* o, float* lse, hipStream_t stream);
 
 /*
  * attn_decode_paged -- multi-token decode over a paged KV cache: every

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     combine_lse,
     decode,
+    decode_noalloc,
     decode_paged,
     decode_splitkv,
     lib,

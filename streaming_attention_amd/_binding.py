@@ -23,7 +23,8 @@ ATTN_DTYPE_BF16 = 1
 _DTYPE_CODE = {torch.float32: ATTN_DTYPE_F32, torch.bfloat16: ATTN_DTYPE_BF16}
 
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
-          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_LAUNCH"}
+          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_WORKSPACE"}
+NOALLOC_MAX_PARTIALS = 65536   # ATTN_NOALLOC_MAX_PARTIALS
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -35,6 +36,7 @@ SIGNATURES = {
     "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], ctypes.c_int),
     "attn_combine_lse": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], ctypes.c_int),
     "attn_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "attn_decode_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], ctypes.c_int),
     "attn_decode_paged": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P],
                           ctypes.c_int),
     "attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -335,6 +337,39 @@ def decode(q, k_cache, v_cache, kv_len=None, num_splits=None, max_splits: int = 
                            B, Hq, Hkv, S_cap, d, int(max_splits), ATTN_DTYPE_BF16, float(scale),
                            _ptr(part_o), _ptr(part_lse), _ptr(counters), _ptr(out), _ptr(lse), _stream(q))
     _check(st, "attn_decode")
+    return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_len=None, num_splits=None, max_splits: int = 64,
+                   scale: float | None = None, out=None, lse=None):
+    """Split-KV decode + merge with the partials in the library's fixed
+    workspace (``attn_decode_noalloc``): the launch itself allocates nothing.
+    Pass ``out [B,Hq,1,d]`` bf16 and ``lse [B,Hq]`` f32 to allocate nothing
+    here either.  Requires ``B * Hq * max_splits <= 65536``.  Calls that
+    overlap in time on one GPU share the workspace and race."""
+    _need(q, "q", 4, torch.bfloat16)
+    _need(k_cache, "k_cache", 4, torch.bfloat16, q.device)
+    _need(v_cache, "v_cache", 4, torch.bfloat16, q.device)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per sequence: q must be [B,Hq,1,d]")
+    Hkv, S_cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, S_cap, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    for name, t in (("kv_len", kv_len), ("num_splits", num_splits)):
+        if t is not None:
+            _need(t, name, 1, torch.int32, q.device, (B,))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", 4, torch.bfloat16, q.device, (B, Hq, 1, d))
+    if lse is not None:
+        _need(lse, "lse", 2, torch.float32, q.device, (B, Hq))
+    st = lib().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(num_splits),
+                                   B, Hq, Hkv, S_cap, d, int(max_splits), ATTN_DTYPE_BF16, float(scale),
+                                   _ptr(out), _ptr(lse), _stream(q))
+    _check(st, "attn_decode_noalloc")
     return out, lse
 
 

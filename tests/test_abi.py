@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_every_entry_point():
     names = declared_functions()
     for n in ("attn_prefill", "attn_prefill_splitkv", "attn_decode_splitkv", "attn_combine_lse", "attn_decode",
-              "attn_decode_paged", "attn_status_string"):
+              "attn_decode_noalloc", "attn_decode_paged", "attn_status_string"):
         assert n in names
 
 
@@ -42,7 +42,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = sa.lib()
-    for code in range(6):
+    for code in range(7):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.attn_status_string(99).decode() == "unknown status"
@@ -110,6 +110,28 @@ def decode_fused(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=10
 ])
 def test_fused_decode_host_validation(kw, expect):
     assert decode_fused(**kw) == expect
+
+
+def decode_noalloc(q=P, k=P, v=P, kv_len=None, ns=None, B=2, Hq=8, Hkv=2, S_cap=100, d=128, max_splits=8,
+                   dtype=BF16, scale=0.088, o=P, lse=P, stream=None):
+    return sa.lib().attn_decode_noalloc(q, k, v, kv_len, ns, B, Hq, Hkv, S_cap, d, max_splits, dtype, scale,
+                                        o, lse, stream)
+
+
+WORKSPACE = 6
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(o=None), NULL), (dict(q=None), NULL), (dict(k=None), NULL),
+    (dict(max_splits=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(scale=-1.0), SHAPE),
+    (dict(dtype=F32), UNSUP), (dict(Hq=64, Hkv=2), UNSUP), (dict(o=MIS), ALIGN), (dict(lse=MIS), ALIGN),
+    (dict(B=0), OK), (dict(B=0, o=None, q=None), OK),
+    (dict(B=16, Hq=64, Hkv=8, max_splits=65), WORKSPACE),       # 16 * 64 * 65 > 65536 partials
+    (dict(B=1 << 12, Hq=16, Hkv=2, max_splits=2), WORKSPACE),
+    (dict(B=16, Hq=64, Hkv=8, max_splits=65, o=None), WORKSPACE),   # the size check comes first
+])
+def test_decode_noalloc_host_validation(kw, expect):
+    assert decode_noalloc(**kw) == expect
 
 
 def combine(po=P, pl=P, ns=None, B=2, Hq=8, max_splits=8, d=128, o=P, lse=P, dtype=BF16, stream=None):
