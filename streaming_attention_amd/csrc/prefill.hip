@@ -14,9 +14,13 @@
 //     when there are enough such blocks to give every CU one, else 4 waves =
 //     128 rows (two workgroups per CU); each wave owns 32 rows.  KV tiles of
 //     64 keys go from global memory straight into LDS (buffer loads with the
-//     LDS destination, no register staging), double buffered: the next tiles'
-//     loads are in flight while the current tile is computed, and one barrier
-//     per tile orders the rings.
+//     LDS destination, no register staging) while earlier tiles are computed.
+//     The 8-wave launches run the two-team kernel (prefill_pp_kernel below):
+//     the two waves of every SIMD alternate between the MFMA work and the
+//     softmax work of their tiles, in step through workgroup barriers.  The
+//     4-wave and paged launches run prefill_bf16_kernel, in which each wave
+//     interleaves both kinds of work itself and one barrier per tile orders
+//     a double-buffered ring.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     K (from LDS) is the A operand and Q (held in VGPRs for the whole sweep)
 //     the B operand.  In the accumulator layout every lane then owns ONE query
@@ -158,6 +162,14 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, lds_t* d
 // Completion of this wave's direct-to-LDS loads (they count as vector memory
 // loads); a workgroup barrier after it publishes the tiles to all waves.
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same wait as a compiler builtin (vmcnt 0, other counters unchanged:
+// gfx9 encoding expcnt 7, lgkmcnt 15), so that the compiler's own wait
+// insertion knows that every earlier vector memory load has completed.
+__device__ __forceinline__ void wait_vm_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 template <int P>
 using Parity = std::integral_constant<int, P>;
@@ -663,6 +675,454 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
 }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel, two-team form (8 waves, 256 stacked rows, one workgroup per CU)
+//
+// Waves w and w + 4 of a workgroup run on the same SIMD.  The waves are two
+// teams -- team 0 = waves 0-3, team 1 = waves 4-7, one wave of each on every
+// SIMD -- that take turns between two phases, with one workgroup barrier
+// between phases ("half-steps"):
+//   matrix phase of tile j: S(j+1) = K(j+1) Q^T and O^T += V(j)^T P(j)^T,
+//                           32 MFMAs per wave at d = 128, operands from LDS;
+//   vector phase of tile j: P(j) = 2^(S(j) c - m), its row sums and bf16
+//                           packing (plus the mask on straddling tiles).
+// Team 0 runs the matrix phase of tile j in half-step 2j and the vector phase
+// of tile j + 1 in half-step 2j + 1; team 1 runs the same one half-step
+// later.  In every half-step each SIMD therefore holds one wave that issues
+// MFMAs back to back and one that does the softmax arithmetic beside them, so
+// the matrix core is fed while the exponentials run, whatever the order the
+// SIMD picks instructions in.  This is the pages' idea of starting the next
+// tile's score GEMM before the current tile's softmax, carried across waves.
+//
+// K and V tiles go through three-slot LDS rings (tile x in slot x % 3).  The
+// loads ride in the vector phases, so a matrix phase issues only LDS reads
+// and MFMAs: team 0 loads K(j+3) during its vector phase of tile j + 1, team
+// 1 loads V(j+2) during its vector phase of tile j, and each team waits for
+// its loads at the end of its next matrix phase, so the barrier that closes
+// that half-step publishes the tile.  Every slot is reloaded only after the
+// barrier that follows its last read (K(j) stays until both teams have run
+// the vector phase of tile j, which may recompute its scores), and a V tile
+// is published one half-step before the first wave that reads it starts its
+// matrix phase: the vector phase reads the first V^T fragment of the wave's
+// next matrix phase ahead, so that phase starts with an MFMA, not with an LDS
+// round trip.  The tile loop is unrolled three times so that every slot index
+// is a compile-time constant: the compiler then tells a read of one slot from
+// a direct load in flight into another and adds no wait for it.
+// ---------------------------------------------------------------------------
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Skv,
+    float c, int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int NW = 8, NT = 64 * NW, BM = 32 * NW;
+  constexpr int RB = 2 * D;                 // bytes per K / V row
+  constexpr int U = D / 8;                  // 16-byte units per row
+  constexpr int TB = kBN * RB;              // bytes per tile
+  constexpr int NLD = kBN * U / NT;         // direct loads per thread per tile (all 8 waves)
+  constexpr int NLT = kBN * U / (NT / 2);   // the same when one team of 4 waves loads a tile
+  constexpr int DS = D / 16;                // MFMA k-steps over d for S^T
+  constexpr int DB = D / 32;                // 32-row d blocks of O^T
+  constexpr int NM = 2 * DS;                // score MFMAs per tile (= P V MFMAs)
+  constexpr int PF = 1;                     // V^T fragments read ahead across the barrier
+  constexpr int LA = 4;                     // MFMAs whose LDS operands are in flight
+  static_assert(NLD * NT == kBN * U && NLT * NT == 2 * kBN * U && NM == 4 * DB && PF <= LA && LA < NM,
+                "tile shape");
+  auto sk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto sv = [](int r) { return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); };
+
+  // V slots first: the transposing V reads (two per MFMA) then all fit the
+  // 16-bit offset field of the LDS instructions, and only the K reads of two
+  // slots need an address add.
+  __shared__ __attribute__((aligned(1024))) char lds_a_v0[TB];
+  __shared__ __attribute__((aligned(1024))) char lds_a_v1[TB];
+  __shared__ __attribute__((aligned(1024))) char lds_a_v2[TB];
+  __shared__ __attribute__((aligned(1024))) char lds_b_k0[TB];
+  __shared__ __attribute__((aligned(1024))) char lds_b_k1[TB];
+  __shared__ __attribute__((aligned(1024))) char lds_b_k2[TB];
+  auto kslot = [&](auto s) __attribute__((always_inline)) -> lds_t* {
+    constexpr int i = decltype(s)::value;
+    return i == 0 ? (lds_t*)lds_b_k0 : (i == 1 ? (lds_t*)lds_b_k1 : (lds_t*)lds_b_k2);
+  };
+  auto vslot = [&](auto s) __attribute__((always_inline)) -> lds_t* {
+    constexpr int i = decltype(s)::value;
+    return i == 0 ? (lds_t*)lds_a_v0 : (i == 1 ? (lds_t*)lds_a_v1 : (lds_t*)lds_a_v2);
+  };
+
+  const int G = Hq / Hkv;
+  const int rows_total = G * Sq;
+  const int n_mt = (rows_total + BM - 1) / BM;
+  const TileCoord tc = map_tile<BM>(blockIdx.x, B * Hkv * n_splits, n_splits, Hkv, n_mt, G, Sq);
+  const int r0 = tc.mt * BM;
+  const int q_start = Skv - Sq;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int team = w >> 2;
+  const int l = tid & 63;
+  const int lr = l & 31;
+  const int hf = l >> 5;
+
+  const size_t head0 = (size_t)tc.b * Hq + (size_t)tc.kvh * G;
+  const bf16* qg = q + head0 * Sq * D;
+  const size_t kvoff = ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
+
+  const int row = r0 + 32 * w + lr;
+  const int pos = q_start + (row < rows_total ? row % Sq : 0);
+
+  // Tile range of the workgroup (its key split, cut at the causal extent),
+  // and the last tile this wave needs (relative to the first, -1 for none).
+  const int tiles_all = (Skv + kBN - 1) / kBN;
+  const int tiles_per_split = (tiles_all + n_splits - 1) / n_splits;
+  int kt_lo = tc.split * tiles_per_split;
+  int kt_hi = min(tiles_all, kt_lo + tiles_per_split);
+  int wave_tmin = 0x3fffffff;
+  int wave_end = 0x3fffffff;
+  if (CAUSAL) {
+    int tmin, tmax;
+    row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, tmin, tmax);
+    const int vis_end = q_start + tmax + 1;
+    kt_hi = min(kt_hi, vis_end > 0 ? (vis_end + kBN - 1) / kBN : 0);
+    const int wA = r0 + 32 * w, wB = min(r0 + 32 * w + 31, rows_total - 1);
+    if (wA <= wB) {
+      int a, bb;
+      row_range_positions(wA, wB, Sq, a, bb);
+      wave_tmin = a;
+      const int wv_end = q_start + bb + 1;
+      wave_end = wv_end > 0 ? (wv_end + kBN - 1) / kBN : 0;
+    }
+  }
+  kt_lo = __builtin_amdgcn_readfirstlane(kt_lo);
+  kt_hi = __builtin_amdgcn_readfirstlane(kt_hi);
+  wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
+  const int T = max(kt_hi - kt_lo, 0);
+  const bool wave_active = r0 + 32 * w < rows_total;
+  const int jw_last = __builtin_amdgcn_readfirstlane(wave_active ? min(min(wave_end, kt_hi) - kt_lo, T) - 1 : -1);
+
+  // Q^T B operands: lane holds Q[row][16 s + 8 hf .. +7]; rows past the last
+  // stacked row read as zero.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)rows_total * D * 2);
+  bf16x8 qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(buf_ld16(rq, (uint32_t)row * D * 2 + 16 * hf + 32 * s, 0));
+  // Waited for here, on every path: the compiler's wait insertion then never
+  // sees these loads pending inside the loop, where a wait on them would also
+  // wait for the tile loads in flight.
+  wait_vm_loads();
+
+  // Direct loads (same unit map and swizzles as the kernel above).
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Skv * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Skv * RB);
+  // Prologue tiles: all 8 waves load, unit p = 64 (8 j + w) + l.  In the loop
+  // one team loads a tile (team 0 the K tiles, team 1 the V tiles): unit
+  // p = 64 (4 j + w % 4) + l.  The source offsets undo the swizzles.
+  auto k_src_of = [&](int p) __attribute__((always_inline)) {
+    const int r = p / U, u = p % U;
+    return (uint32_t)(r * RB + 16 * (u ^ sk(r)));
+  };
+  auto v_src_of = [&](int p) __attribute__((always_inline)) {
+    const int r = p / U, u = p % U;
+    return (uint32_t)(r * RB + 32 * ((u >> 1) ^ sv(r)) + 16 * (u & 1));
+  };
+  auto load_k = [&](int kt, lds_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+      load_to_lds16(rk, dst + 1024 * (NW * j + w), k_src_of(64 * (NW * j + w) + l), (uint32_t)kt * TB);
+  };
+  auto load_v = [&](int kt, lds_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+      load_to_lds16(rv, dst + 1024 * (NW * j + w), v_src_of(64 * (NW * j + w) + l), (uint32_t)kt * TB);
+  };
+  const int wt = w & 3;   // wave index inside its team
+  uint32_t t_src[NLT];    // this wave's source offsets for its team's tile (K for team 0, V for team 1)
+#pragma unroll
+  for (int j = 0; j < NLT; ++j) {
+    const int p = 64 * (4 * j + wt) + l;
+    t_src[j] = team == 0 ? k_src_of(p) : v_src_of(p);
+  }
+  auto load_team = [&](int kt, lds_t* dst) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = team == 0 ? rk : rv;
+#pragma unroll
+    for (int j = 0; j < NLT; ++j) load_to_lds16(r, dst + 1024 * (4 * j + wt), t_src[j], (uint32_t)kt * TB);
+  };
+
+  // Operand read offsets (as in the kernel above).
+  uint32_t k_rd[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) k_rd[s] = (uint32_t)(lr * RB + 16 * ((2 * s + hf) ^ sk(lr)));
+  const int g4 = l >> 4, jj = l & 15;
+  const int vrow = 4 * (g4 >> 1) + (jj >> 2);
+  uint32_t v_rd[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    v_rd[db] = (uint32_t)(vrow * RB + 32 * ((2 * db + (g4 & 1)) ^ sv(vrow)) + 8 * (jj & 3));
+
+  float m_run = kNegInf, l_run = 0.f;
+  // Rescale of O owed by a raised exponent base, applied at the start of the
+  // next matrix phase (rescaling in the vector phase costs the compiler's
+  // register allocation more than the loop has).
+  float o_corr = 1.f;
+  bool o_pending = false;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
+  f32x16 S[2];
+  bf16x8 pf[2][2];
+  bf16x8 pre_v[PF];   // operands of the first PF MFMAs of the next matrix phase
+
+  // Operand fragments: score MFMA i is d step i / 2, key block i % 2; P V
+  // MFMA i is key chunk (i / (2 DB), (i / DB) % 2), d block i % DB.
+  auto k_frag = [&](const lds_t* Ks, int i) __attribute__((always_inline)) { return lds_read16(Ks + 32 * (i & 1) * RB + k_rd[i >> 1]); };
+  auto v_frag = [&](const lds_t* Vs, int i) __attribute__((always_inline)) {
+    const int kb = i / (2 * DB), cc = (i / DB) & 1, db = i % DB;
+    const lds_t* vp = Vs + (32 * kb + 16 * cc) * RB + v_rd[db];
+    const s16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * RB);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto mfma_s = [&](const bf16x8& a, int i) __attribute__((always_inline)) {
+    const int kb = i & 1;
+    S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1], (i >> 1) == 0 ? f32x16{} : S[kb], 0, 0, 0);
+  };
+  auto mfma_pv = [&](const bf16x8& a, int i) __attribute__((always_inline)) {
+    const int kb = i / (2 * DB), cc = (i / DB) & 1, db = i % DB;
+    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][cc], oacc[db], 0, 0, 0);
+  };
+  // Operand of MFMA t of a matrix phase: t < NM the P V MFMA t (V slot Vs),
+  // else the score MFMA t - NM (K slot Ks).
+  auto frag = [&](const lds_t* Ks, const lds_t* Vs, int t) __attribute__((always_inline)) {
+    return t < NM ? v_frag(Vs, t) : k_frag(Ks, t - NM);
+  };
+  auto prefetch = [&](const lds_t* Vs) __attribute__((always_inline)) {
+    // Issued after the vector work, not hoisted into it: the fragments then
+    // hold registers only across the barrier.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) pre_v[i] = v_frag(Vs, i);
+  };
+  // Matrix phase: the P V MFMAs of the current tile (V slot Vs, P in pf),
+  // then the score MFMAs of the next tile (K slot Ks) into S.  P is dead
+  // before S is written, so the two never hold registers at once; the LDS
+  // reads run LA MFMAs ahead of their use.  After a wave's last tile the
+  // scores are computed from whatever the slot holds and never used: one code
+  // path keeps the compiler's register allocation of the loop simple.
+  auto matrix_phase = [&](const lds_t* Ks, const lds_t* Vs) __attribute__((always_inline)) {
+    if (o_pending) {   // rare: the vector phase raised the exponent base
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[i][j] *= o_corr;
+      o_corr = 1.f;
+      o_pending = false;
+    }
+    __builtin_amdgcn_s_setprio(1);
+    constexpr int NT2 = 2 * NM;
+    bf16x8 fr[NT2];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) fr[t] = pre_v[t];
+#pragma unroll
+    for (int t = PF; t < LA; ++t) fr[t] = frag(Ks, Vs, t);
+#pragma unroll
+    for (int t = 0; t < NT2; ++t) {
+      if (t + LA < NT2) fr[t + LA] = frag(Ks, Vs, t + LA);
+      if (t < NM) mfma_pv(fr[t], t);
+      else mfma_s(fr[t], t - NM);
+    }
+    // Schedule: the reads of MFMAs PF .. LA - 1 first (two LDS reads for a
+    // V^T fragment, one for a K fragment), then each MFMA after the reads
+    // of the MFMA LA places later.
+    constexpr int lead = (LA <= NM ? 2 * (LA - PF) : 2 * (NM - PF) + (LA - NM));
+    if (lead > 0) __builtin_amdgcn_sched_group_barrier(0x100, lead, 0);
+#pragma unroll
+    for (int t = 0; t < NT2; ++t) {
+      if (t + LA < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (t + LA < NT2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto mask_tile = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const bool vis = (key < Skv) && (!CAUSAL || key <= pos);
+        S[kb][r] = vis ? S[kb][r] : kNegInf;
+      }
+  };
+  auto tile_needs_mask = [&](int kt) __attribute__((always_inline)) {
+    const int key_end = kt * kBN + kBN - 1;
+    return (key_end >= Skv) || (CAUSAL && key_end > q_start + wave_tmin);
+  };
+  // P = 2^(S c - m) in place, this lane's partial row sum, and the bf16 P^T
+  // operands (slot e' of chunk (kb, cc) is key 32 kb + 16 cc + 8 (e' / 4) +
+  // 4 hf + e' % 4, i.e. accumulator register 8 cc + e').
+  auto exponentiate = [&]() __attribute__((always_inline)) {
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[kb][r] = exp2_hw(__builtin_fmaf(S[kb][r], c, -m_use));
+    return sum_tree32(S[0], S[1]);
+  };
+  auto pack = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int r8 = 8 * cc;
+        pf[kb][cc] = to_bf16x8(S[kb][r8 + 0], S[kb][r8 + 1], S[kb][r8 + 2], S[kb][r8 + 3], S[kb][r8 + 4],
+                               S[kb][r8 + 5], S[kb][r8 + 6], S[kb][r8 + 7]);
+      }
+  };
+  // Rare path (the fixed exponent base of the kernel above): the row sums of
+  // the tile grew past kSumCap, so the scores are recomputed from K, still in
+  // its LDS slot Ks, the base is raised to the tile's max and l rescaled (O
+  // when the matrix phase next runs).
+  auto redo_tile = [&](int kt, const lds_t* Ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) mfma_s(k_frag(Ks, i), i);
+    if (tile_needs_mask(kt)) mask_tile(kt);
+    const float m_new = fmaxf(m_run, max_xor32(max_of32(S[0], S[1])) * c);
+    const float corr = (m_new == kNegInf) ? 1.f : exp2_hw(m_run - m_new);
+    l_run *= corr;
+    o_corr *= corr;   // O is rescaled before its next P V product
+    o_pending = true;
+    m_run = m_new;
+  };
+  auto vector_phase = [&](int kt, const lds_t* Ks) __attribute__((always_inline)) {
+    if (__builtin_expect(tile_needs_mask(kt), 0)) mask_tile(kt);
+    float psum = exponentiate();
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kSumCap))) {   // also catches inf / NaN
+      redo_tile(kt, Ks);
+      psum = exponentiate();
+    }
+    pack();
+    l_run += psum;
+  };
+  // Workgroup barrier that the compiler may not move memory operations across
+  // (s_barrier alone does not order them), with no wait on loads in flight.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (T > 0) {
+    // Prologue: K(0..2) and V(0..1) in flight together; S(0) and the exponent
+    // base (its row max) for every wave; team 0 also takes the softmax of
+    // tile 0 here, team 1 in half-step 0.
+    load_k(kt_lo, kslot(IC<0>{}));
+    if (T > 1) load_k(kt_lo + 1, kslot(IC<1>{}));
+    if (T > 2) load_k(kt_lo + 2, kslot(IC<2>{}));
+    load_v(kt_lo, vslot(IC<0>{}));
+    if (T > 1) load_v(kt_lo + 1, vslot(IC<1>{}));
+    wait_vm_loads();
+    barrier();
+    if (jw_last >= 0) {
+#pragma unroll
+      for (int i = 0; i < NM; ++i) mfma_s(k_frag(kslot(IC<0>{}), i), i);
+      if (tile_needs_mask(kt_lo)) mask_tile(kt_lo);
+      m_run = max_xor32(max_of32(S[0], S[1])) * c;
+      if (team == 0) {
+        vector_phase(kt_lo, kslot(IC<0>{}));
+        prefetch(vslot(IC<0>{}));
+      }
+    }
+  }
+
+  // One tile j of a team's loop: two half-steps.  Team 0: matrix phase of
+  // tile j, then vector phase of tile j + 1; team 1: vector phase of tile j,
+  // then matrix phase of tile j.  The loads ride in the vector phases, so the
+  // matrix phases issue nothing but LDS reads and MFMAs: team 0 loads K(j+3)
+  // in half-step 2j + 1, team 1 loads V(j+2) in half-step 2j, and each team
+  // waits for its loads at the end of its next matrix phase, so the barrier
+  // that closes that half-step publishes the tile.  JM = j % 3 names the
+  // slots.
+  auto tile_team0 = [&](auto jm, int j) __attribute__((always_inline)) {
+    constexpr int JM = decltype(jm)::value;
+    if (j <= jw_last) matrix_phase(kslot(IC<(JM + 1) % 3>{}), vslot(IC<JM>{}));
+    wait_vm_loads();
+    barrier();
+    if (j + 3 < T) load_team(kt_lo + j + 3, kslot(IC<JM>{}));
+    if (j + 1 <= jw_last) {
+      vector_phase(kt_lo + j + 1, kslot(IC<(JM + 1) % 3>{}));
+      prefetch(vslot(IC<(JM + 1) % 3>{}));
+    }
+    barrier();
+  };
+  auto tile_team1 = [&](auto jm, int j) __attribute__((always_inline)) {
+    constexpr int JM = decltype(jm)::value;
+    if (j + 2 < T) load_team(kt_lo + j + 2, vslot(IC<(JM + 2) % 3>{}));
+    if (j <= jw_last) {
+      vector_phase(kt_lo + j, kslot(IC<JM>{}));
+      prefetch(vslot(IC<JM>{}));
+    }
+    barrier();
+    if (j <= jw_last) matrix_phase(kslot(IC<(JM + 1) % 3>{}), vslot(IC<JM>{}));
+    wait_vm_loads();
+    barrier();
+  };
+  // The loop runs a whole number of 3-tile rounds: tiles past the last do
+  // nothing but keep the barriers in step.
+  if (team == 0) {
+    for (int j = 0; j < T; j += 3) {
+      tile_team0(IC<0>{}, j);
+      tile_team0(IC<1>{}, j + 1);
+      tile_team0(IC<2>{}, j + 2);
+    }
+  } else {
+    for (int j = 0; j < T; j += 3) {
+      tile_team1(IC<0>{}, j);
+      tile_team1(IC<1>{}, j + 1);
+      tile_team1(IC<2>{}, j + 2);
+    }
+  }
+
+  // Epilogue (as in the kernel above).
+  const float l_tot = sum_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_row = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  if (row < rows_total) {
+    const size_t flat = head0 * Sq + row;
+    if (part_o != nullptr) {
+      const size_t slot = flat * n_splits + tc.split;
+      float* prow = part_o + slot * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hf;
+          f32x4 val = {oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                       oacc[db][4 * q4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(prow + d0) = val;
+        }
+      if (hf == 0) part_lse[slot] = lse_row;
+    } else {
+      bf16* orow = o + flat * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hf;
+          const uint32_t lo = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 0] * inv)),
+                                      __builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 1] * inv)));
+          const uint32_t hi = pack_lo(__builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 2] * inv)),
+                                      __builtin_bit_cast(uint16_t, (bf16)(oacc[db][4 * q4 + 3] * inv)));
+          u32x2 pr = {lo, hi};
+          *reinterpret_cast<u32x2*>(orow + d0) = pr;
+        }
+      if (lse != nullptr && hf == 0) lse[flat] = lse_row;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel
 // ---------------------------------------------------------------------------
 constexpr int kBN32 = 32;   // keys per KV tile (fp32 path)
@@ -835,7 +1295,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     // MFMA but spill at one wave per SIMD: the compiler shuttles the output
     // accumulators between AGPRs and VGPRs.)  8 waves (256 rows) per
     // workgroup, one workgroup per CU, whenever that still gives every CU a
-    // workgroup: each K/V tile brought into LDS then serves twice the rows.
+    // workgroup: each K/V tile brought into LDS then serves twice the rows,
+    // and the two-team kernel runs (paged mode keeps the one-team kernel).
     // Smaller problems take 4-wave workgroups, two per CU.
     const long long wg8 = (rows + 255) / 256 * groups * a.n_splits;
     const bool eight = rows > 128 && wg8 >= kNumCUs;
@@ -847,12 +1308,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                      (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, c, \
                      a.n_splits, a.part_o, a.part_lse, a.block_table, a.kv_len, a.max_pages, a.num_pages, \
                      a.seq_splits)
+#define SA_LAUNCH_PP(DD, CC)                                                                             \
+  hipLaunchKernelGGL((prefill_pp_kernel<DD, CC>), g, blk_w, 0, stream, (const bf16*)a.q, (const bf16*)a.k, \
+                     (const bf16*)a.v, (bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, c, a.n_splits,    \
+                     a.part_o, a.part_lse)
 #define SA_LAUNCH_BF16(DD, CC)                                                                           \
   do {                                                                                                   \
     if (paged) {                                                                                         \
       if (eight) SA_LAUNCH_ONE(DD, CC, 8, true); else SA_LAUNCH_ONE(DD, CC, 4, true);                   \
     } else {                                                                                             \
-      if (eight) SA_LAUNCH_ONE(DD, CC, 8, false); else SA_LAUNCH_ONE(DD, CC, 4, false);                 \
+      if (eight) SA_LAUNCH_PP(DD, CC); else SA_LAUNCH_ONE(DD, CC, 4, false);                            \
     }                                                                                                    \
   } while (0)
     if (a.d == 128) {
@@ -861,6 +1326,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
       if (a.causal) SA_LAUNCH_BF16(64, true); else SA_LAUNCH_BF16(64, false);
     }
 #undef SA_LAUNCH_BF16
+#undef SA_LAUNCH_PP
 #undef SA_LAUNCH_ONE
   } else {
     const dim3 g((unsigned)((rows + kBM - 1) / kBM * groups));
