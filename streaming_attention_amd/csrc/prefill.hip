@@ -998,11 +998,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   auto vector_phase = [&](int kt, const lds_t* Ks) __attribute__((always_inline)) {
     if (__builtin_expect(tile_needs_mask(kt), 0)) mask_tile(kt);
     float psum = exponentiate();
+    // Packed before the range check, so that the packing overlaps the row-sum
+    // tree instead of waiting for the check; the rare redo packs again.
+    pack();
     if (__builtin_amdgcn_ballot_w64(!(psum <= kSumCap))) {   // also catches inf / NaN
       redo_tile(kt, Ks);
       psum = exponentiate();
+      pack();
     }
-    pack();
     l_run += psum;
   };
   // Workgroup barrier that the compiler may not move memory operations across

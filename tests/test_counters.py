@@ -3,36 +3,69 @@
 profiles/)."""
 
 # SQ_INSTS_MFMA of one 70B-shape causal prefill launch (B=1, 64/8 heads,
-# S=8192, d=128), profiles/prefill_lds_mfma_counters_70b.md.
-MEASURED_PREFILL_MFMA = 34_537_472
-# FETCH_SIZE (KiB, copy-calibrated x2) of the decode split kernel and the KV
-# bytes it must read, profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
+# S=8192, d=128; two-team kernel), profiles/prefill_lds_mfma_counters_70b.md.
+MEASURED_PREFILL_MFMA = 34_078_720
+# FETCH_SIZE and WRITE_SIZE (KiB per launch) of the same launch, and the
+# copy calibration (FETCH_SIZE reads half the bytes a plain copy moves,
+# WRITE_SIZE all of them), profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
+MEASURED_PREFILL_FETCH_KIB = 137_604
+MEASURED_PREFILL_WRITE_KIB = 133_188
+FETCH_SCALE, WRITE_SCALE = 0.5, 1.0
+# FETCH_SIZE (KiB) of the decode split kernel and the KV bytes it must read.
 MEASURED_DECODE_FETCH_KIB = 262_469
 DECODE_KV_BYTES = 4 * 8 * 32768 * 128 * 2 * 2
 
+PREFILL_B, PREFILL_HQ, PREFILL_HKV, PREFILL_S, PREFILL_D = 1, 64, 8, 8192, 128
+
 
 def prefill_mfma_count(S, G, Hkv, rows_per_wg=256, waves=8, key_tile=64, d=128):
-    """MFMA instructions of a causal prefill (Sq = Skv = S): per wave, the
-    first tile's scores, then one step per key tile up to the wave's last
-    visible tile (score MFMAs of the next tile + P V MFMAs of the previous
-    one), then the last tile's P V product if the wave reaches it."""
+    """MFMA instructions of a causal prefill (Sq = Skv = S) in the two-team
+    kernel: per wave, the scores of the first key tile, then one matrix phase
+    per key tile the wave sees (the P V product of that tile and the scores of
+    the next, computed even after the wave's last tile)."""
     per_tile = 2 * (d // 16)          # 32x32x16 MFMAs for 64 keys x 32 rows (scores), and as many for P V
+    rows = rows_per_wg // waves
     total = 0
     for _ in range(Hkv * G):
         for t0 in range(0, S, rows_per_wg):
-            kt_hi = -(-(t0 + rows_per_wg) // key_tile)
             for w in range(waves):
-                rows = rows_per_wg // waves
-                wave_end = min(-(-(t0 + rows * (w + 1)) // key_tile), kt_hi)
-                steps = min(wave_end, kt_hi - 1) + 1
-                total += per_tile + 2 * per_tile * steps + (per_tile if wave_end >= kt_hi else 0)
+                tiles = -(-(t0 + rows * (w + 1)) // key_tile)   # causal: keys up to the wave's last row
+                total += per_tile + 2 * per_tile * tiles
     return total
 
 
+def prefill_algorithmic_bytes():
+    """Q, K, V read once; O (bf16) and LSE (fp32) written once."""
+    q = PREFILL_B * PREFILL_HQ * PREFILL_S * PREFILL_D * 2
+    kv = 2 * PREFILL_B * PREFILL_HKV * PREFILL_S * PREFILL_D * 2
+    o = q
+    lse = PREFILL_B * PREFILL_HQ * PREFILL_S * 4
+    return q, kv, o + lse
+
+
 def test_prefill_issues_exactly_the_mfmas_of_its_causal_schedule():
-    assert prefill_mfma_count(8192, 8, 8) == MEASURED_PREFILL_MFMA
+    assert prefill_mfma_count(PREFILL_S, PREFILL_HQ // PREFILL_HKV, PREFILL_HKV) == MEASURED_PREFILL_MFMA
+
+
+def test_prefill_hbm_traffic_stays_within_one_and_a_half_times_the_minimum():
+    q, kv, out = prefill_algorithmic_bytes()
+    fetched = MEASURED_PREFILL_FETCH_KIB * 1024 / FETCH_SCALE
+    written = MEASURED_PREFILL_WRITE_KIB * 1024 / WRITE_SCALE
+    assert fetched >= q + kv and written >= out                      # nothing is read or written less than once
+    assert fetched + written <= 1.5 * (q + kv + out)
+    assert written <= 1.01 * out                                    # O and LSE written once
+
+
+def test_prefill_kv_reads_share_the_group():
+    """The G = 8 query heads of a KV head read its K/V tiles together (one
+    workgroup holds 256 stacked rows of one KV head), so the K/V bytes fetched
+    from memory stay far below one fetch per query head."""
+    q, kv, _ = prefill_algorithmic_bytes()
+    kv_fetched = MEASURED_PREFILL_FETCH_KIB * 1024 / FETCH_SCALE - q
+    G = PREFILL_HQ // PREFILL_HKV
+    assert kv_fetched <= 5 * kv < G * kv
 
 
 def test_decode_fetches_each_kv_byte_once():
-    fetched = MEASURED_DECODE_FETCH_KIB * 1024 * 2          # FETCH_SIZE counts half the bytes (copy calibration)
+    fetched = MEASURED_DECODE_FETCH_KIB * 1024 / FETCH_SCALE
     assert DECODE_KV_BYTES <= fetched <= 1.002 * DECODE_KV_BYTES
