@@ -20,7 +20,8 @@ own and reported under their own keys:
   * `paged_decode`: multi-token decode over a paged cache (16 sequences x 4
     tokens, lengths 1K-32K).
 Kernel times come from HIP events recorded on the stream the kernels run on,
-over the timed steps.  The float64 oracle, timed on
+over the timed steps; the events are created with hipEventDisableSystemFence
+(timing only, no system-scope cache writeback at each record, see Timer).  The float64 oracle, timed on
 the host cores on a bounded sample of the same prefill workload, is reported as
 `cpu_baseline` (a baseline only).
 
@@ -152,24 +153,95 @@ def cpu_baseline(target_s: float):
     }
 
 
-def timed_mean_ms(fn, warmup: int, steps: int, stream) -> float:
+class Timer:
+    """Timing events on the launch stream.
+
+    The events are HIP events created with hipEventDisableSystemFence, on the
+    HIP runtime the process already has loaded (the one torch uses).  A
+    default event's recording releases at system scope, which writes back and
+    invalidates the GPU caches; the kernel that follows then starts late and
+    on cold caches, and that cost lands in the next timing window (measured:
+    +2 to 3 us on the 93 us decode after the prefill).  HIP documents the flag
+    for exactly this use: events that only time work.  If the runtime cannot
+    be found, torch's default events are used and the JSON says so."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream):
+        import ctypes
+        import re
+
+        import torch
+
+        self.stream = stream
+        self.hip = None
+        try:
+            maps = open("/proc/self/maps", encoding="utf-8").read()
+            paths = sorted(set(re.findall(r"(/\S*libamdhip64\S*)", maps)))
+            if paths:
+                hip = ctypes.CDLL(paths[0], mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+                for name in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventSynchronize",
+                             "hipEventElapsedTime", "hipEventDestroy"):
+                    getattr(hip, name).restype = ctypes.c_int
+                self.hip = hip
+        except OSError:
+            self.hip = None
+        self._ctypes = ctypes
+        self._torch = torch
+        self._live = []
+        self.kind = ("HIP events with hipEventDisableSystemFence on the launch stream" if self.hip is not None
+                     else "torch.cuda.Event on the launch stream (HIP runtime not found)")
+
+    def event(self):
+        if self.hip is None:
+            return self._torch.cuda.Event(enable_timing=True)
+        e = self._ctypes.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self._ctypes.byref(e), self._ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self._live.append(e)
+        return e
+
+    def record(self, e):
+        if self.hip is None:
+            e.record(self.stream)
+        elif self.hip.hipEventRecord(e, self._ctypes.c_void_p(self.stream.cuda_stream)):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        if self.hip is None:
+            return a.elapsed_time(b)
+        if self.hip.hipEventSynchronize(b):
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = self._ctypes.c_float()
+        if self.hip.hipEventElapsedTime(self._ctypes.byref(ms), a, b):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        if self.hip is not None:
+            for e in self._live:
+                self.hip.hipEventDestroy(e)
+        self._live = []
+
+
+def timed_mean_ms(fn, warmup: int, steps: int, timer: Timer) -> float:
     """Mean time of one call of fn over `steps` calls after `warmup` untimed
-    ones: HIP events recorded on the launch stream around the timed calls."""
+    ones: timing events recorded on the launch stream around the timed calls."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    e0, e1 = timer.event(), timer.event()
+    timer.record(e0)
     for _ in range(steps):
         fn()
-    e1.record(stream)
+    timer.record(e1)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return timer.elapsed_ms(e0, e1) / steps
 
 
-def measure_ragged(sa, W, dev, stream, warmup, steps):
+def measure_ragged(sa, W, dev, timer, warmup, steps):
     """Ragged decode: B=16, lengths uniform in [1024, 131072] from the seed,
     splits per length (splits_for_lengths), split-KV + merge."""
     import torch
@@ -186,7 +258,7 @@ def measure_ragged(sa, W, dev, stream, warmup, steps):
     def call():
         sa.decode(qr, kr, vr, lens_d, ns_d, max_splits=64, scale=wr.scale, part_o=po, part_lse=pl, out=o, lse=lse)
 
-    ms = timed_mean_ms(call, warmup, steps, stream)
+    ms = timed_mean_ms(call, warmup, steps, timer)
     kv = W.decode_kv_bytes(lens_r, wr.Hkv, wr.d)
     gbs = kv / (ms * 1e-3) / 1e9
     return {"workload": f"ragged split-KV decode B={wr.B} Hq={wr.Hq} Hkv={wr.Hkv} d={wr.d} bf16, lengths "
@@ -200,7 +272,7 @@ def measure_ragged(sa, W, dev, stream, warmup, steps):
                          "traffic_unit": "HBM bytes per call, split + merge (fetch + write)"}}
 
 
-def measure_mha(sa, W, dev, stream, warmup, steps):
+def measure_mha(sa, W, dev, timer, warmup, steps):
     """Causal MHA prefill B=2, H=16, S=1024, d=64 (bf16): report only."""
     import torch
 
@@ -209,7 +281,7 @@ def measure_mha(sa, W, dev, stream, warmup, steps):
     om = torch.empty_like(qm)
     lsem = torch.empty((wm.B, wm.Hq, wm.Sq), dtype=torch.float32, device=dev)
     ms = timed_mean_ms(lambda: sa.prefill(qm, km, vm, causal=True, scale=wm.scale, out=om, lse=lsem),
-                       warmup, steps, stream)
+                       warmup, steps, timer)
     tf = wm.flops() / (ms * 1e-3) / 1e12
     return {"workload": f"causal MHA prefill B={wm.B} H={wm.Hq} S={wm.Sq} d={wm.d} bf16 (report only)",
             "kernels": "prefill_bf16_kernel<64,causal>", "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
@@ -254,8 +326,9 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
+    timer = Timer(stream)
     n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    ev = [[timer.event() for _ in range(3)] for _ in range(n_ev)]
 
     do_pf = args.only in ("all", "prefill")
     do_dc = args.only in ("all", "decode")
@@ -266,16 +339,16 @@ def main():
 
     def step(i=None):
         if i is not None:
-            ev[i][0].record(stream)
+            timer.record(ev[i][0])
         if do_pf:
             sa.prefill(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
         if i is not None:
-            ev[i][1].record(stream)
+            timer.record(ev[i][1])
         if do_dc:
             sa.decode(qd, kc, vc, None, None, max_splits=wd.splits, scale=wd.scale,
                       part_o=part_o, part_lse=part_lse, out=od, lse=lsed)
         if i is not None:
-            ev[i][2].record(stream)
+            timer.record(ev[i][2])
 
     wall = 0.0
     if do_pf or do_dc:
@@ -290,18 +363,18 @@ def main():
 
     pf_ms = dc_ms = float("nan")
     if do_pf or do_dc:
-        pf_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)) / n_ev
-        dc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)) / n_ev
+        pf_ms = sum(timer.elapsed_ms(ev[i][0], ev[i][1]) for i in range(n_ev)) / n_ev
+        dc_ms = sum(timer.elapsed_ms(ev[i][1], ev[i][2]) for i in range(n_ev)) / n_ev
     ms_step = wall * 1e3 / args.steps
 
     ragged = None
     if do_rg:   # ragged split-KV decode + merge, timed on its own (not part of the step)
-        ragged = measure_ragged(sa, W, dev, stream, args.warmup, args.steps)
+        ragged = measure_ragged(sa, W, dev, timer, args.warmup, args.steps)
         torch.cuda.empty_cache()
 
     mha = None
     if do_mh:
-        mha = measure_mha(sa, W, dev, stream, args.warmup, args.steps)
+        mha = measure_mha(sa, W, dev, timer, args.warmup, args.steps)
 
     chunked = None
     if do_ch:   # split-KV prefill + merge, timed on its own (not part of the step)
@@ -310,16 +383,8 @@ def main():
         oc = torch.empty_like(qc)
         lsec = torch.empty((wc.B, wc.Hq, wc.Sq), dtype=torch.float32, device=dev)
         n_sp = sa.prefill_splits(wc.B, wc.Hq, wc.Hkv, wc.Sq, wc.Skv)
-        for _ in range(args.warmup):
-            sa.prefill(qc, kc2, vc2, causal=True, scale=wc.scale, out=oc, lse=lsec)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            sa.prefill(qc, kc2, vc2, causal=True, scale=wc.scale, out=oc, lse=lsec)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ch_ms = e0.elapsed_time(e1) / args.steps
+        ch_ms = timed_mean_ms(lambda: sa.prefill(qc, kc2, vc2, causal=True, scale=wc.scale, out=oc, lse=lsec),
+                              args.warmup, args.steps, timer)
         ch_tf = wc.flops() / (ch_ms * 1e-3) / 1e12
         chunked = {"workload": f"causal chunked prefill B={wc.B} Hq={wc.Hq} Hkv={wc.Hkv} Sq={wc.Sq} "
                                f"Skv={wc.Skv} (query block after a {wc.Skv - wc.Sq}-token prefix) d={wc.d} bf16",
@@ -339,16 +404,8 @@ def main():
         og = torch.empty((wg.B, wg.Hq, wg.T_q, wg.d), dtype=torch.bfloat16, device=dev)
         lseg = torch.empty((wg.B, wg.Hq, wg.T_q), dtype=torch.float32, device=dev)
         n_sp = sa.paged_splits(wg.B, wg.Hq, wg.Hkv, wg.T_q, tbl.shape[1])
-        for _ in range(args.warmup):
-            sa.decode_paged(qg, kpg, vpg, tbl_d, lens_d, scale=wg.scale, out=og, lse=lseg)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            sa.decode_paged(qg, kpg, vpg, tbl_d, lens_d, scale=wg.scale, out=og, lse=lseg)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        pg_ms = e0.elapsed_time(e1) / args.steps
+        pg_ms = timed_mean_ms(lambda: sa.decode_paged(qg, kpg, vpg, tbl_d, lens_d, scale=wg.scale, out=og, lse=lseg),
+                              args.warmup, args.steps, timer)
         pg_bytes = W.decode_kv_bytes(lens_g, wg.Hkv, wg.d)
         pg_gbs = pg_bytes / (pg_ms * 1e-3) / 1e9
         paged = {"workload": f"multi-token decode over a paged cache: B={wg.B} T_q={wg.T_q} Hq={wg.Hq} Hkv={wg.Hkv} "
@@ -416,6 +473,7 @@ def main():
             "algorithmic_bytes": kv_bytes,
         },
         "device": torch.cuda.get_device_name(dev),
+        "timer": timer.kind,
     }
     if ragged is not None:
         result["ragged_decode"] = ragged
@@ -428,6 +486,7 @@ def main():
     if not args.no_cpu_baseline:
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    timer.close()
     print(json.dumps(result), flush=True)
 
 
