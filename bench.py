@@ -388,7 +388,7 @@ def main():
         ch_tf = wc.flops() / (ch_ms * 1e-3) / 1e12
         chunked = {"workload": f"causal chunked prefill B={wc.B} Hq={wc.Hq} Hkv={wc.Hkv} Sq={wc.Sq} "
                                f"Skv={wc.Skv} (query block after a {wc.Skv - wc.Sq}-token prefix) d={wc.d} bf16",
-                   "kv_splits": n_sp, "kernels": "prefill_bf16_kernel<128,causal> (split-KV) + combine_lse",
+                   "kv_splits": n_sp, "kernels": "prefill_pp_kernel<128,causal> (split-KV, two-team) + combine_lse",
                    "ms": round(ch_ms, 4), "tflops": round(ch_tf, 2),
                    "pct_mfma_peak": round(100 * ch_tf / MFMA_BF16_PEAK_TFLOPS, 2),
                    "algorithmic_tflop": round(wc.flops() / 1e12, 6),
@@ -451,7 +451,7 @@ def main():
                    "pct_hbm_peak": round(100 * dc_gbs / HBM_PEAK_GBS, 2)},
         "roofline": {
             "bound": "mfma",
-            "kernel": "prefill_bf16_kernel<128,causal>",
+            "kernel": "prefill_pp_kernel<128,causal> (two-team, 8-wave workgroups)",
             "achieved": round(pf_tflops, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",

@@ -849,9 +849,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   };
 
   // Operand read offsets (as in the kernel above).
+  // K read offsets carry a bias of kKBias that the reads take back in their
+  // constant part: the K slots then sit within the 16-bit offset field of the
+  // LDS reads from a per-lane base, with no address add per read.  (The empty
+  // asm hides the bias from the compiler, which would fold it back.)
+  constexpr uint32_t kKBias = 32768;
   uint32_t k_rd[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) k_rd[s] = (uint32_t)(lr * RB + 16 * ((2 * s + hf) ^ sk(lr)));
+  for (int s = 0; s < DS; ++s) {
+    k_rd[s] = kKBias + (uint32_t)(lr * RB + 16 * ((2 * s + hf) ^ sk(lr)));
+    asm("" : "+v"(k_rd[s]));
+  }
   const int g4 = l >> 4, jj = l & 15;
   const int vrow = 4 * (g4 >> 1) + (jj >> 2);
   uint32_t v_rd[DB];
@@ -860,6 +868,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     v_rd[db] = (uint32_t)(vrow * RB + 32 * ((2 * db + (g4 & 1)) ^ sv(vrow)) + 8 * (jj & 3));
 
   float m_run = kNegInf, l_run = 0.f;
+  float m_use = 0.f;   // the exponent base as applied: m_run, or 0 while no key was seen
   // Rescale of O owed by a raised exponent base, applied at the start of the
   // next matrix phase (rescaling in the vector phase costs the compiler's
   // register allocation more than the loop has).
@@ -876,7 +885,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
 
   // Operand fragments: score MFMA i is d step i / 2, key block i % 2; P V
   // MFMA i is key chunk (i / (2 DB), (i / DB) % 2), d block i % DB.
-  auto k_frag = [&](const lds_t* Ks, int i) __attribute__((always_inline)) { return lds_read16(Ks + 32 * (i & 1) * RB + k_rd[i >> 1]); };
+  auto k_frag = [&](const lds_t* Ks, int i) __attribute__((always_inline)) {
+    return lds_read16(Ks + ((int)(32 * (i & 1) * RB) - (int)kKBias) + k_rd[i >> 1]);
+  };
   auto v_frag = [&](const lds_t* Vs, int i) __attribute__((always_inline)) {
     const int kb = i / (2 * DB), cc = (i / DB) & 1, db = i % DB;
     const lds_t* vp = Vs + (32 * kb + 16 * cc) * RB + v_rd[db];
@@ -963,7 +974,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   // operands (slot e' of chunk (kb, cc) is key 32 kb + 16 cc + 8 (e' / 4) +
   // 4 hf + e' % 4, i.e. accumulator register 8 cc + e').
   auto exponentiate = [&]() __attribute__((always_inline)) {
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -994,13 +1004,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     o_corr *= corr;   // O is rescaled before its next P V product
     o_pending = true;
     m_run = m_new;
+    m_use = (m_run == kNegInf) ? 0.f : m_run;
   };
   auto vector_phase = [&](int kt, const lds_t* Ks) __attribute__((always_inline)) {
     if (__builtin_expect(tile_needs_mask(kt), 0)) mask_tile(kt);
     float psum = exponentiate();
     // Packed before the range check, so that the packing overlaps the row-sum
-    // tree instead of waiting for the check; the rare redo packs again.
+    // tree instead of waiting for the check; the rare redo packs again.  (The
+    // empty asm takes the packed operands, which keeps the compiler from
+    // moving the packing past the branch.)
     pack();
+    asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
     if (__builtin_amdgcn_ballot_w64(!(psum <= kSumCap))) {   // also catches inf / NaN
       redo_tile(kt, Ks);
       psum = exponentiate();
@@ -1016,10 +1030,18 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     asm volatile("" ::: "memory");
   };
 
+  // Loads of one ring tile by this wave's team: team 0 fills the K ring,
+  // team 1 the V ring (a uniform branch, so that each load names its slot).
+  auto load_ring = [&](auto slot, int kt) __attribute__((always_inline)) {
+    if (team == 0) load_team(kt, kslot(slot));
+    else load_team(kt, vslot(slot));
+  };
+
   if (T > 0) {
     // Prologue: K(0..2) and V(0..1) in flight together; S(0) and the exponent
-    // base (its row max) for every wave; team 0 also takes the softmax of
-    // tile 0 here, team 1 in half-step 0.
+    // base (its row max) for every wave, then the softmax of tile 0.  Team 1
+    // runs that softmax as its first half-step (beside team 0's first matrix
+    // phase) and loads V(2) in it; team 0 runs it before its first half-step.
     load_k(kt_lo, kslot(IC<0>{}));
     if (T > 1) load_k(kt_lo + 1, kslot(IC<1>{}));
     if (T > 2) load_k(kt_lo + 2, kslot(IC<2>{}));
@@ -1027,65 +1049,49 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     if (T > 1) load_v(kt_lo + 1, vslot(IC<1>{}));
     wait_vm_loads();
     barrier();
+    if (team == 1 && T > 2) load_team(kt_lo + 2, vslot(IC<2>{}));
     if (jw_last >= 0) {
 #pragma unroll
       for (int i = 0; i < NM; ++i) mfma_s(k_frag(kslot(IC<0>{}), i), i);
       if (tile_needs_mask(kt_lo)) mask_tile(kt_lo);
       m_run = max_xor32(max_of32(S[0], S[1])) * c;
-      if (team == 0) {
-        vector_phase(kt_lo, kslot(IC<0>{}));
-        prefetch(vslot(IC<0>{}));
-      }
+      m_use = (m_run == kNegInf) ? 0.f : m_run;
+      vector_phase(kt_lo, kslot(IC<0>{}));
+      prefetch(vslot(IC<0>{}));
     }
+    if (team == 1) barrier();
   }
 
-  // One tile j of a team's loop: two half-steps.  Team 0: matrix phase of
-  // tile j, then vector phase of tile j + 1; team 1: vector phase of tile j,
-  // then matrix phase of tile j.  The loads ride in the vector phases, so the
-  // matrix phases issue nothing but LDS reads and MFMAs: team 0 loads K(j+3)
-  // in half-step 2j + 1, team 1 loads V(j+2) in half-step 2j, and each team
-  // waits for its loads at the end of its next matrix phase, so the barrier
-  // that closes that half-step publishes the tile.  JM = j % 3 names the
-  // slots.
-  auto tile_team0 = [&](auto jm, int j) __attribute__((always_inline)) {
+  // One tile j of the loop, the same code for both teams: the matrix phase of
+  // tile j, then the vector phase of tile j + 1, one half-step each.  Team 1
+  // runs one half-step behind team 0, so in every half-step one team is in a
+  // matrix phase and the other in a vector phase.  The loads ride in the
+  // vector phases, so the matrix phases issue nothing but LDS reads and
+  // MFMAs: in its vector phase of tile j + 1 a team loads tile j + 3 of its
+  // ring into slot j % 3, and it waits for those loads at the end of its next
+  // matrix phase, so the barrier that closes that half-step publishes the
+  // tile.  JM = j % 3 names the slots.
+  auto tile = [&](auto jm, int j) __attribute__((always_inline)) {
     constexpr int JM = decltype(jm)::value;
     if (j <= jw_last) matrix_phase(kslot(IC<(JM + 1) % 3>{}), vslot(IC<JM>{}));
     wait_vm_loads();
     barrier();
-    if (j + 3 < T) load_team(kt_lo + j + 3, kslot(IC<JM>{}));
+    if (j + 3 < T) load_ring(IC<JM>{}, kt_lo + j + 3);
     if (j + 1 <= jw_last) {
       vector_phase(kt_lo + j + 1, kslot(IC<(JM + 1) % 3>{}));
       prefetch(vslot(IC<(JM + 1) % 3>{}));
     }
     barrier();
   };
-  auto tile_team1 = [&](auto jm, int j) __attribute__((always_inline)) {
-    constexpr int JM = decltype(jm)::value;
-    if (j + 2 < T) load_team(kt_lo + j + 2, vslot(IC<(JM + 2) % 3>{}));
-    if (j <= jw_last) {
-      vector_phase(kt_lo + j, kslot(IC<JM>{}));
-      prefetch(vslot(IC<JM>{}));
-    }
-    barrier();
-    if (j <= jw_last) matrix_phase(kslot(IC<(JM + 1) % 3>{}), vslot(IC<JM>{}));
-    wait_vm_loads();
-    barrier();
-  };
   // The loop runs a whole number of 3-tile rounds: tiles past the last do
-  // nothing but keep the barriers in step.
-  if (team == 0) {
-    for (int j = 0; j < T; j += 3) {
-      tile_team0(IC<0>{}, j);
-      tile_team0(IC<1>{}, j + 1);
-      tile_team0(IC<2>{}, j + 2);
-    }
-  } else {
-    for (int j = 0; j < T; j += 3) {
-      tile_team1(IC<0>{}, j);
-      tile_team1(IC<1>{}, j + 1);
-      tile_team1(IC<2>{}, j + 2);
-    }
+  // nothing but keep the barriers in step.  Team 0 ends with one barrier
+  // more, matching team 1's first half-step.
+  for (int j = 0; j < T; j += 3) {
+    tile(IC<0>{}, j);
+    tile(IC<1>{}, j + 1);
+    tile(IC<2>{}, j + 2);
   }
+  if (team == 0 && T > 0) barrier();
 
   // Epilogue (as in the kernel above).
   const float l_tot = sum_xor32(l_run);
