@@ -57,14 +57,14 @@ METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQ
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "f3693b6303cf74eb",
-                "fetch_kib": 137604, "write_kib": 133188},
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "d5b3b49c61659a93",
+                "fetch_kib": 137513, "write_kib": 133120},
     "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "e2f749b667918352",
                "fetch_kib": 262472 + 4174, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "27c35c287acb491d",
-                "fetch_kib": 140548 + 16917, "write_kib": 33289 + 8448},
-    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "27c35c287acb491d",
-              "fetch_kib": 592156 + 8277, "write_kib": 17409 + 1056},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "d901896ff99407cb",
+                "fetch_kib": 140441 + 16917, "write_kib": 33280 + 8448},
+    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "d901896ff99407cb",
+              "fetch_kib": 592154 + 8277, "write_kib": 17409 + 1056},
     "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "e2f749b667918352",
                "fetch_kib": 2032436 + 8206, "write_kib": 17141 + 288},
 }
