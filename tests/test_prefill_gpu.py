@@ -305,6 +305,49 @@ def test_eight_wave_launch_rows_of_every_tile(B, Hq, Hkv, Sq, Skv, d, causal):
     check_prefill_rows(o, lse, q, k, v, scale, causal, rows)
 
 
+# The 8-wave (two-team) launch over short key ranges: one to five 64-key
+# tiles, fewer than the loop's three-slot rings hold, so the prologue, the
+# second team's first half-step and the idle tail half-steps all run.  Every
+# output element is checked.
+EIGHT_WAVE_SHORT = [
+    # B, Hq, Hkv, Sq, Skv, d, causal
+    (16, 64, 8, 64, 64, 128, True),       # one tile
+    (16, 64, 8, 64, 128, 128, False),     # two tiles
+    (16, 64, 8, 100, 150, 128, True),     # three tiles, ragged last tile and query block
+    (16, 64, 8, 64, 250, 64, False),      # four tiles, d = 64
+    (16, 64, 8, 40, 300, 128, True),      # five tiles, each wave ending at a different tile
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal", EIGHT_WAVE_SHORT)
+def test_eight_wave_launch_short_key_ranges(B, Hq, Hkv, Sq, Skv, d, causal):
+    assert -(-(Hq // Hkv) * Sq // 256) * B * Hkv >= 256 and (Hq // Hkv) * Sq > 128   # 8-wave workgroups
+    assert sa.prefill_splits(B, Hq, Hkv, Sq, Skv) == 1
+    g = torch.Generator(device=DEV).manual_seed(4000 + Sq + Skv + d)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    run_and_check(q, k, v, causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("step", [2.0, -1.0])
+def test_eight_wave_scores_that_climb_or_fall_across_tiles(step, causal):
+    """As the drift test above, in the 8-wave (two-team) launch: there the
+    range guard's redo reads the tile's K back from its LDS slot while the
+    other team runs, and the owed O rescale is applied in the next matrix
+    phase."""
+    B, Hq, Hkv, Sq, Skv, d = 16, 64, 8, 64, 600, 128
+    assert -(-(Hq // Hkv) * Sq // 256) * B * Hkv >= 256 and sa.prefill_splits(B, Hq, Hkv, Sq, Skv) == 1
+    g = torch.Generator(device=DEV).manual_seed(int(100 * step) + 7 + causal)
+    q = (1.0 + 0.25 * torch.randn((B, Hq, Sq, d), generator=g, device=DEV)).to(torch.bfloat16)
+    drift = step * (torch.arange(Skv, device=DEV) // 64).float()
+    k = (drift[None, None, :, None] + 0.25 * torch.randn((B, Hkv, Skv, d), generator=g, device=DEV)).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    o, lse = run_and_check(q, k, v, causal)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
 def test_lse_output_is_optional():
     """lse = NULL writes O only, bitwise the same O as with the LSE output (both
     launch shapes: 4-wave small, 8-wave large)."""
