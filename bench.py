@@ -57,16 +57,16 @@ METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQ
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "d5b3b49c61659a93",
-                "fetch_kib": 137513, "write_kib": 133120},
-    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "e2f749b667918352",
-               "fetch_kib": 262472 + 4174, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "d901896ff99407cb",
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "c8c1c32ab3672969",
+                "fetch_kib": 137511, "write_kib": 133120},
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "ef81d625a0761543",
+               "fetch_kib": 262469 + 4174, "write_kib": 8704 + 72},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "aecdb15188972ca5",
                 "fetch_kib": 140441 + 16917, "write_kib": 33280 + 8448},
-    "paged": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "d901896ff99407cb",
-              "fetch_kib": 592154 + 8277, "write_kib": 17409 + 1056},
-    "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "e2f749b667918352",
-               "fetch_kib": 2032436 + 8206, "write_kib": 17141 + 288},
+    "paged": {"sources": ["common.h", "paged.hip", "combine.hip"], "sha256_16": "fa1fead7b5579044",
+              "fetch_kib": 574406 + 6261, "write_kib": 12392 + 1056},
+    "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "ef81d625a0761543",
+               "fetch_kib": 2032434 + 8206, "write_kib": 17138 + 288},
 }
 
 
@@ -412,7 +412,7 @@ def main():
                              f"d={wg.d} bf16, lengths U[{wg.len_lo},{wg.len_hi}] (sum {int(lens_g.sum())}), "
                              f"pages of {wg.page} shuffled in the pool",
                  "kv_splits": n_sp,
-                 "kernels": "prefill_bf16_kernel<128,causal,paged> (split-KV) + combine_lse",
+                 "kernels": "decode_paged_bf16_kernel<128> (split-KV) + combine_lse",
                  "us": round(pg_ms * 1e3, 2), "kv_gbs": round(pg_gbs, 1),
                  "pct_hbm_peak": round(100 * pg_gbs / HBM_PEAK_GBS, 2), "kv_bytes": pg_bytes,
                  "traffic": measured_traffic("paged"),

@@ -377,17 +377,25 @@ PAGE = 64   # positions per KV-cache page (the kernels' key tile)
 
 
 def paged_splits(B: int, Hq: int, Hkv: int, T_q: int, max_pages: int) -> int:
-    """Default split count of ``decode_paged``, the same for every sequence:
-    about 1024 (query block, split) workgroups -- four per compute unit, so
-    the short sequences' small workgroups fill in around the long ones --
-    keeping at least 8 pages of the longest possible sequence per split.
-    Measured on 16 sequences of 1K-32K keys: 8 splits beat both fewer and
-    more, and beat splits sized per sequence.  Any split count gives the same
-    result up to rounding."""
-    blocks = -(-(Hq // Hkv) * T_q // 128) * B * Hkv
+    """Default split count of ``decode_paged``, the same for every sequence.
+
+    Query blocks of at most 32 stacked rows (G * T_q <= 32) run the streaming
+    paged decode kernel, two workgroups per compute unit: aim at about 768
+    (sequence, KV head, split) workgroups, three per compute unit, so that
+    the short sequences' workgroups fill in around the long ones.  Larger
+    query blocks run the prefill kernel's paged mode: about 1024 (query
+    block, split) workgroups.  Either way at least 8 pages of the longest
+    possible sequence go to a split.  Measured on 16 sequences of 1K-32K keys
+    (8 heads x 4 tokens): 6 splits beat 4, 8, 10, 12 and 16, and beat splits
+    sized per sequence.  Any split count gives the same result up to rounding."""
+    rows = (Hq // Hkv) * T_q
+    if rows <= 32:
+        blocks, target = B * Hkv, 768
+    else:
+        blocks, target = -(-rows // 128) * B * Hkv, 1024
     if blocks == 0:
         return 1
-    return int(max(1, min(-(-1024 // blocks), max_pages // 8, 256)))
+    return int(max(1, min(-(-target // blocks), max_pages // 8, 256)))
 
 
 def decode_paged(q, k_pages, v_pages, block_table, kv_len, num_splits: int | None = None,

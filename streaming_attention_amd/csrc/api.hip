@@ -183,7 +183,9 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
   a.part_lse = num_splits > 1 ? part_lse : nullptr;
   a.block_table = block_table; a.kv_len = kv_len; a.max_pages = max_pages; a.num_pages = num_pages;
   a.seq_splits = num_splits > 1 ? num_splits_seq : nullptr;
-  return sa::launch_prefill(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  const hipError_t e = sa::decode_paged_fits(Hq, Hkv, T_q, d) ? sa::launch_decode_paged(a, stream)
+                                                               : sa::launch_prefill(a, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,

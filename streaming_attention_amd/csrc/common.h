@@ -120,4 +120,41 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// LDS pointers and 16-byte / transposing LDS reads.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_t;
+
+__device__ __forceinline__ bf16x8 lds_read16(const lds_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+// ds_read_b64_tr_b16: in every 16-lane group, lane i receives element i % 4 of
+// the 8 bytes addressed by lane 4 e + i / 4, as its element e.
+__device__ __forceinline__ s16x4 lds_read_tr16(const lds_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(p)));
+}
+
+// Longest sequences first (paged decode): slot r of the launch goes to the
+// sequence of rank r by valid length, longest first, ties by index, so the
+// workgroups with the most keys start first and the short ones fill the tail.
+// The B <= kRankMax clamped lengths are staged in LDS (len_s) and every thread
+// ranks its sequences against all of them; beyond kRankMax sequences, launch
+// order.  Every thread of the workgroup calls it (it synchronises).
+constexpr int kRankMax = 256;
+template <int NT>
+__device__ __forceinline__ int seq_of_rank(const int32_t* kv_len, int B, int cap, int r, int* len_s, int* pick) {
+  if (B > kRankMax) return r;
+  auto clamp_len = [&](int len) { return len < 0 ? 0 : (len > cap ? cap : len); };
+  for (int j = threadIdx.x; j < B; j += NT) len_s[j] = clamp_len(kv_len[j]);
+  __syncthreads();
+  for (int j = threadIdx.x; j < B; j += NT) {
+    const int lj = len_s[j];
+    int rank = 0;
+    for (int i = 0; i < B; ++i) rank += (len_s[i] > lj) || (len_s[i] == lj && i < j);
+    if (rank == r) *pick = j;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*pick);
+}
+
 }  // namespace sa

@@ -60,5 +60,10 @@ struct CombineArgs {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine_lse(const CombineArgs& a, hipStream_t stream);
+// Paged multi-token decode for small query blocks (G * T_q <= 32, d 64 or 128):
+// the streaming decode kernel; other paged shapes run the prefill kernel's
+// paged mode (launch_prefill with block_table set).
+bool decode_paged_fits(int Hq, int Hkv, int T_q, int d);
+hipError_t launch_decode_paged(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace sa

@@ -62,7 +62,6 @@ constexpr int kNumCUs = 256;          // MI355X compute units
 constexpr float kSumCap = 16777216.f;  // 2^24: largest partial row sum of P accepted without
                                       // raising the exponent base (P <= 2^24 keeps O far from fp32 overflow)
 constexpr int kLdsAhead = 4;          // LDS operand reads issued ahead of their MFMA
-constexpr int kRankMax = 256;         // paged mode: most sequences ordered by length
 
 struct TileCoord {
   int b, kvh, mt, split;
@@ -143,16 +142,6 @@ __device__ __forceinline__ void row_range_positions(int rA, int rB, int Sq, int&
 // fragment read from LDS would feed two MFMAs) at one wave per SIMD, but it
 // spills under the compiler's register allocation; the launches use QB = 1.
 // ---------------------------------------------------------------------------
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_t;
-
-__device__ __forceinline__ bf16x8 lds_read16(const lds_t* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
-}
-__device__ __forceinline__ s16x4 lds_read_tr16(const lds_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(p)));
-}
 // 16 bytes per lane, global (buffer, byte offset voff + soff) -> LDS chunk dst
 // (wave-uniform; lane l writes dst + 16 l).  Out-of-range bytes arrive as zero.
 __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint32_t voff, uint32_t soff) {
@@ -225,28 +214,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   TileCoord tc = map_tile<BM>(blockIdx.x, n_groups * n_splits, n_splits, Hkv, n_mt, G, Sq);
   const int r0 = tc.mt * BM;
   if constexpr (PAGED) {
-    auto clamp_len = [&](int len) { return len < 0 ? 0 : (len > kBN * max_pages ? kBN * max_pages : len); };
-    // Longest sequences first: map_tile deals the sequence slots in launch
-    // order, and slot r goes to the sequence of rank r by length (ties by
-    // index), so the workgroups with the most tiles start first and the short
-    // ones fill the tail.  Up to kRankMax sequences (beyond that, launch
-    // order); the lengths are staged in LDS and every thread ranks its
-    // sequences against all of them.
-    if (B <= kRankMax) {
-      __shared__ int len_s[kRankMax];
-      __shared__ int pick;
-      for (int j = threadIdx.x; j < B; j += NT) len_s[j] = clamp_len(kv_len[j]);
-      __syncthreads();
-      for (int j = threadIdx.x; j < B; j += NT) {
-        const int lj = len_s[j];
-        int rank = 0;
-        for (int i = 0; i < B; ++i) rank += (len_s[i] > lj) || (len_s[i] == lj && i < j);
-        if (rank == tc.b) pick = j;
-      }
-      __syncthreads();
-      tc.b = __builtin_amdgcn_readfirstlane(pick);
-    }
-    Skv = clamp_len(kv_len[tc.b]);   // keys of this workgroup's sequence
+    // map_tile deals the sequence slots in launch order; slot r is the
+    // sequence of rank r by length, longest first.
+    __shared__ int len_s[kRankMax];
+    __shared__ int pick;
+    const int cap = kBN * max_pages;
+    tc.b = seq_of_rank<NT>(kv_len, B, cap, tc.b, len_s, &pick);
+    const int len = kv_len[tc.b];
+    Skv = len < 0 ? 0 : (len > cap ? cap : len);   // keys of this workgroup's sequence
   }
   const int q_start = Skv - Sq;
 

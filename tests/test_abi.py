@@ -200,9 +200,10 @@ def test_prefill_splits_heuristic():
 
 
 def test_paged_splits_heuristic():
-    assert sa.paged_splits(16, 64, 8, 4, 512) == 8      # 128 query blocks -> 8 splits
-    assert sa.paged_splits(1, 64, 8, 1, 4096) == 128    # one sequence: split its keys widely
+    assert sa.paged_splits(16, 64, 8, 4, 512) == 6      # 32 stacked rows, 128 (sequence, KV head) pairs -> 6 splits
+    assert sa.paged_splits(1, 64, 8, 1, 4096) == 96     # one sequence: split its keys widely
     assert sa.paged_splits(64, 64, 8, 4, 8) == 1        # 512 keys at most: no split
+    assert sa.paged_splits(4, 64, 8, 16, 512) == 32     # 128 stacked rows (the prefill kernel's paged mode): 32 blocks -> 1024 / 32
 
 
 def test_splits_for_lengths():

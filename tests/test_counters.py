@@ -8,12 +8,18 @@ MEASURED_PREFILL_MFMA = 34_078_720
 # FETCH_SIZE and WRITE_SIZE (KiB per launch) of the same launch, and the
 # copy calibration (FETCH_SIZE reads half the bytes a plain copy moves,
 # WRITE_SIZE all of them), profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
-MEASURED_PREFILL_FETCH_KIB = 137_513
+MEASURED_PREFILL_FETCH_KIB = 137_511
 MEASURED_PREFILL_WRITE_KIB = 133_120
 FETCH_SCALE, WRITE_SCALE = 0.5, 1.0
 # FETCH_SIZE (KiB) of the decode split kernel and the KV bytes it must read.
 MEASURED_DECODE_FETCH_KIB = 262_469
 DECODE_KV_BYTES = 4 * 8 * 32768 * 128 * 2 * 2
+# FETCH_SIZE (KiB) of the paged decode kernel (16 sequences x 4 tokens, 64/8
+# heads, lengths summing to 286,824 keys, 64-position pages shuffled in the
+# pool), the K/V bytes of the valid keys and the Q bytes.
+MEASURED_PAGED_FETCH_KIB = 574_406
+PAGED_KV_BYTES = 286_824 * 8 * 128 * 2 * 2
+PAGED_Q_BYTES = 16 * 64 * 4 * 128 * 2
 
 PREFILL_B, PREFILL_HQ, PREFILL_HKV, PREFILL_S, PREFILL_D = 1, 64, 8, 8192, 128
 
@@ -69,3 +75,10 @@ def test_prefill_kv_reads_share_the_group():
 def test_decode_fetches_each_kv_byte_once():
     fetched = MEASURED_DECODE_FETCH_KIB * 1024 / FETCH_SCALE
     assert DECODE_KV_BYTES <= fetched <= 1.002 * DECODE_KV_BYTES
+
+
+def test_paged_decode_fetches_each_valid_kv_byte_once():
+    """Pages are read only up to each sequence's length (rows past it in the
+    last page are never fetched) and each valid K/V byte once."""
+    fetched = MEASURED_PAGED_FETCH_KIB * 1024 / FETCH_SCALE
+    assert PAGED_KV_BYTES <= fetched <= 1.002 * (PAGED_KV_BYTES + PAGED_Q_BYTES)
