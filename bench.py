@@ -58,15 +58,15 @@ FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
     "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "c8c1c32ab3672969",
-                "fetch_kib": 137511, "write_kib": 133120},
-    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "ef81d625a0761543",
-               "fetch_kib": 262469 + 4174, "write_kib": 8704 + 72},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "aecdb15188972ca5",
-                "fetch_kib": 140441 + 16917, "write_kib": 33280 + 8448},
-    "paged": {"sources": ["common.h", "paged.hip", "combine.hip"], "sha256_16": "fa1fead7b5579044",
-              "fetch_kib": 574406 + 6261, "write_kib": 12392 + 1056},
-    "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "ef81d625a0761543",
-               "fetch_kib": 2032434 + 8206, "write_kib": 17138 + 288},
+                "fetch_kib": 137551, "write_kib": 133120},
+    "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "05ddfcb1dded8f23",
+               "fetch_kib": 262253 + 4170, "write_kib": 8256 + 65},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "5836a015aefe78e9",
+                "fetch_kib": 140441 + 16914, "write_kib": 33280 + 8448},
+    "paged": {"sources": ["common.h", "paged.hip", "combine.hip"], "sha256_16": "f2459d9c52b18dfe",
+              "fetch_kib": 574406 + 6258, "write_kib": 12391 + 1056},
+    "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "05ddfcb1dded8f23",
+               "fetch_kib": 2031568 + 8203, "write_kib": 16268 + 260},
 }
 
 

@@ -9,7 +9,7 @@
 // valid merge order.
 //
 // MI355X mapping.  Many splits (split-KV decode: tens of splits, few rows):
-// one workgroup (4 waves) per output row.  The kernel is latency-bound (a few
+// one workgroup (4 waves) per output row, row blocks of 8 placed by XCD.  The kernel is latency-bound (a few
 // MB in total), so every load of a row is issued in one round: the split lse
 // values (one per thread, for the workgroup max M) and, per wave, up to 16
 // partial rows (splits w, w + 4, ...; each lane owns D / 64 output elements).
@@ -37,7 +37,15 @@ __global__ __launch_bounds__(256) void combine_lse_kernel(const float* __restric
   __shared__ float acc_s[kWaves][D];
   __shared__ float wsum_s[kWaves];
 
-  const int row = blockIdx.x;
+  // Row block rb of 8 consecutive rows runs on XCD rb % 8 when the rows come
+  // in multiples of 64 (workgroups are dealt to the 8 XCDs round robin): with
+  // 8 query heads per KV head that is the XCD whose L2 holds the rows'
+  // partials from the split-KV decode.
+  int row = blockIdx.x;
+  if ((gridDim.x & 63) == 0) {
+    const int xcd = row & 7, j = row >> 3;
+    row = 8 * (8 * (j >> 3) + xcd) + (j & 7);
+  }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int b = row / Hq;
   int n = num_splits ? num_splits[b] : max_splits;

@@ -9,7 +9,8 @@
 // (m_i, l_i, O_i)), section 2.1 (splits are contiguous key blocks).
 //
 // MI355X mapping
-//   * One workgroup per (sequence, KV head, split), 4 waves.  The split's keys
+//   * One workgroup per (sequence, KV head, split), 4 waves, the splits of a
+//     (sequence, KV head) on one XCD when the groups divide evenly.  The split's keys
 //     are taken 32 at a time; wave w handles chunks w, w + 4, ...  Each wave
 //     keeps its own running (m, l, O) and double-buffers its next chunk's K and
 //     V in registers (non-temporal loads: every byte is read exactly once), so
@@ -157,7 +158,15 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_splitkv_bf16_kernel(
   constexpr int SMEM_BYTES = SMEM_BYTES_VT > MERGE_FLOATS * 4 ? SMEM_BYTES_VT : MERGE_FLOATS * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
 
-  const int wg = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round robin.  When the (sequence, KV
+  // head) groups come in multiples of 8, every split of group gi runs on XCD
+  // gi % 8, so a group's key range streams through one XCD and its partials
+  // sit in that XCD's L2 for the merge (which places its row blocks to match).
+  int wg = blockIdx.x;
+  if (((gridDim.x / max_splits) & 7) == 0) {
+    const int xcd = wg & 7, j = wg >> 3;
+    wg = (8 * (j / max_splits) + xcd) * max_splits + j % max_splits;
+  }
   const int s = wg % max_splits;
   const int kvh = (wg / max_splits) % Hkv;
   const int b = wg / (max_splits * Hkv);

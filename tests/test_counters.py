@@ -8,11 +8,11 @@ MEASURED_PREFILL_MFMA = 34_078_720
 # FETCH_SIZE and WRITE_SIZE (KiB per launch) of the same launch, and the
 # copy calibration (FETCH_SIZE reads half the bytes a plain copy moves,
 # WRITE_SIZE all of them), profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
-MEASURED_PREFILL_FETCH_KIB = 137_511
+MEASURED_PREFILL_FETCH_KIB = 137_551
 MEASURED_PREFILL_WRITE_KIB = 133_120
 FETCH_SCALE, WRITE_SCALE = 0.5, 1.0
 # FETCH_SIZE (KiB) of the decode split kernel and the KV bytes it must read.
-MEASURED_DECODE_FETCH_KIB = 262_469
+MEASURED_DECODE_FETCH_KIB = 262_253
 DECODE_KV_BYTES = 4 * 8 * 32768 * 128 * 2 * 2
 # FETCH_SIZE (KiB) of the paged decode kernel (16 sequences x 4 tokens, 64/8
 # heads, lengths summing to 286,824 keys, 64-position pages shuffled in the
