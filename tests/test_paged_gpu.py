@@ -170,3 +170,47 @@ def test_sequences_sharing_prefix_pages():
     o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), num_splits=2, scale=scale)
     torch.cuda.synchronize()
     _check(o, lse, q, kp, vp, table, lens, scale, range(B))
+
+
+@pytest.mark.parametrize("step", [2.0, -1.0])
+def test_paged_scores_that_climb_or_fall_across_chunks(step):
+    """Key rows drift along the query direction by `step` per 32 positions, so
+    later chunks' scores rise far above (2.0: ~16 log2 units a chunk) or fall
+    below the first chunk's: the streaming paged kernel's range guard must
+    raise the exponent base (recomputing a chunk from its K in LDS) and still
+    give the exact softmax.  8 heads x 4 tokens = 32 stacked rows; pages
+    shuffled in the pool."""
+    w = dataclasses.replace(W.PAGED_DECODE, B=3, Hq=16, Hkv=2, T_q=4, d=128, seed=900 + int(10 * step))
+    assert (w.Hq // w.Hkv) * w.T_q == 32
+    lens = torch.tensor([900, 333, 70], dtype=torch.int32)
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=lens)
+    q = (1.0 + 0.25 * q.float()).to(torch.bfloat16)
+    # Rewrite every valid key with its drift: sequence position p -> step * (p // 32) + noise.
+    for b in range(w.B):
+        n = int(lens_t[b])
+        for p_ in range(-(-n // 64)):
+            slot = int(table[b, p_])
+            pos = torch.arange(64 * p_, 64 * p_ + 64, device=DEV)
+            drift = (step * (pos // 32)).float()[None, :, None]
+            valid = (pos < n)[None, :, None]
+            noise = 0.25 * kp[slot].float().nan_to_num(0.0)
+            kp[slot] = torch.where(valid, drift + noise, kp[slot].float()).to(torch.bfloat16)
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=2, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(w.B))
+
+
+@pytest.mark.parametrize("Hq,Hkv,T_q,d", [(24, 2, 2, 64), (8, 1, 3, 128), (20, 4, 5, 128)])
+def test_paged_partial_row_blocks(Hq, Hkv, T_q, d):
+    """Stacked blocks of 24, 24 and 25 rows (fewer than the 32 the streaming
+    paged kernel holds): the padding rows are computed and never written."""
+    w = dataclasses.replace(W.PAGED_DECODE, B=4, Hq=Hq, Hkv=Hkv, T_q=T_q, d=d, seed=1000 + Hq + T_q + d)
+    assert 16 < (Hq // Hkv) * T_q < 32
+    lens = torch.tensor([400, 3, 64, 1000], dtype=torch.int32)
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=lens)
+    o = torch.full(tuple(q.shape), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(tuple(q.shape[:3]), float("nan"), dtype=torch.float32, device=DEV)
+    sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=3, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(w.B))
