@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * kPW, 2) void decode_paged_bf16_kernel(
 
   const int nch = __builtin_amdgcn_readfirstlane((hi - lo + kPC - 1) / kPC);
   if (nch > 0) {
-    // Q^T B operands: lane holds Q[row lr][16 s + 8 hf .. + 7]; zero past R.
+    // Q^T B operands: lane holds Q[row lr][16 st + 8 hf .. + 7]; zero past R.
     bf16x8 qf[DS];
     const bf16* qrow = q + (row_ok ? flat_row(lr) : 0) * D;
 #pragma unroll
