@@ -12,7 +12,9 @@
 // MI355X mapping (bf16 path)
 //   * One workgroup = 8 waves = 256 stacked query rows of one (batch, KV head)
 //     when there are enough such blocks to give every CU one, else 4 waves =
-//     128 rows (two workgroups per CU); each wave owns 32 rows.  KV tiles of
+//     128 rows (two workgroups per CU); each wave owns 32 rows.  In the 8-wave
+//     launch with G a multiple of 8 the 256 rows are the same 32 positions of
+//     8 query heads, so all waves see the same causal extent.  KV tiles of
 //     64 keys go from global memory straight into LDS (buffer loads with the
 //     LDS destination, no register staging) while earlier tiles are computed.
 //     The 8-wave launches run the two-team kernel (prefill_pp_kernel below):
@@ -98,6 +100,29 @@ __device__ __forceinline__ TileCoord map_tile(int wg, int n_groups, int n_splits
   t.b = group / Hkv;
   t.kvh = group % Hkv;
   t.mt = mt;
+  return t;
+}
+
+// The same dealing for the two-team kernel's head-interleaved blocks (G a
+// multiple of 8): block (hb, pb) holds positions 32 pb .. 32 pb + 31 of query
+// heads 8 hb .. 8 hb + 7; the latest positions are dealt first.
+__device__ __forceinline__ TileCoord map_tile_heads8(int wg, int n_groups, int n_splits, int Hkv, int n_hb,
+                                                     int n_pb) {
+  int group, rk;
+  if ((n_groups & 7) == 0) {
+    const int xcd = wg & 7, slot = wg >> 3, gpx = n_groups >> 3;
+    group = (slot % gpx) * 8 + xcd;
+    rk = slot / gpx;
+  } else {
+    group = wg % n_groups;
+    rk = wg / n_groups;
+  }
+  TileCoord t;
+  t.mt = (rk % n_hb) * n_pb + (n_pb - 1 - rk / n_hb);
+  t.split = group % n_splits;
+  group /= n_splits;
+  t.b = group / Hkv;
+  t.kvh = group % Hkv;
   return t;
 }
 
@@ -727,9 +752,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
 
   const int G = Hq / Hkv;
   const int rows_total = G * Sq;
-  const int n_mt = (rows_total + BM - 1) / BM;
-  const TileCoord tc = map_tile<BM>(blockIdx.x, B * Hkv * n_splits, n_splits, Hkv, n_mt, G, Sq);
-  const int r0 = tc.mt * BM;
+  // Row blocks.  With G a multiple of 8 a block is 32 positions of 8 query
+  // heads, wave w taking head 8 hb + w: every wave then has the same causal
+  // extent, so no SIMD idles through the block's last tiles while another
+  // finishes.  Otherwise a block is 256 consecutive stacked rows (g-major).
+  const bool heads8 = (G & 7) == 0;
+  const int n_pb = (Sq + 31) >> 5;
+  const TileCoord tc =
+      heads8 ? map_tile_heads8(blockIdx.x, B * Hkv * n_splits, n_splits, Hkv, G >> 3, n_pb)
+             : map_tile<BM>(blockIdx.x, B * Hkv * n_splits, n_splits, Hkv, (rows_total + BM - 1) / BM, G, Sq);
   const int q_start = Skv - Sq;
 
   const int tid = threadIdx.x;
@@ -743,8 +774,24 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   const bf16* qg = q + head0 * Sq * D;
   const size_t kvoff = ((size_t)tc.b * Hkv + tc.kvh) * (size_t)Skv * D;
 
-  const int row = r0 + 32 * w + lr;
-  const int pos = q_start + (row < rows_total ? row % Sq : 0);
+  // This wave's first stacked row (g Sq + t) and its number of valid rows, and
+  // the smallest and largest position t of the whole block.
+  int wrow0, wrows, blk_tmin, blk_tmax;
+  if (heads8) {
+    const int t0 = 32 * (tc.mt % n_pb);
+    wrow0 = (8 * (tc.mt / n_pb) + w) * Sq + t0;
+    wrows = min(32, Sq - t0);
+    blk_tmin = t0;
+    blk_tmax = t0 + wrows - 1;
+  } else {
+    const int r0 = tc.mt * BM;
+    wrow0 = r0 + 32 * w;
+    wrows = max(0, min(32, rows_total - wrow0));
+    row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, blk_tmin, blk_tmax);
+  }
+  const int row = wrow0 + lr;
+  const bool row_ok = lr < wrows;
+  const int pos = q_start + (row_ok ? row % Sq : 0);
 
   // Tile range of the workgroup (its key split, cut at the causal extent),
   // and the last tile this wave needs (relative to the first, -1 for none).
@@ -755,14 +802,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   int wave_tmin = 0x3fffffff;
   int wave_end = 0x3fffffff;
   if (CAUSAL) {
-    int tmin, tmax;
-    row_range_positions(r0, min(r0 + BM - 1, rows_total - 1), Sq, tmin, tmax);
-    const int vis_end = q_start + tmax + 1;
+    const int vis_end = q_start + blk_tmax + 1;
     kt_hi = min(kt_hi, vis_end > 0 ? (vis_end + kBN - 1) / kBN : 0);
-    const int wA = r0 + 32 * w, wB = min(r0 + 32 * w + 31, rows_total - 1);
-    if (wA <= wB) {
+    if (wrows > 0) {
       int a, bb;
-      row_range_positions(wA, wB, Sq, a, bb);
+      row_range_positions(wrow0, wrow0 + wrows - 1, Sq, a, bb);
       wave_tmin = a;
       const int wv_end = q_start + bb + 1;
       wave_end = wv_end > 0 ? (wv_end + kBN - 1) / kBN : 0;
@@ -772,19 +816,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   kt_hi = __builtin_amdgcn_readfirstlane(kt_hi);
   wave_tmin = __builtin_amdgcn_readfirstlane(wave_tmin);
   const int T = max(kt_hi - kt_lo, 0);
-  const bool wave_active = r0 + 32 * w < rows_total;
-  const int jw_last = __builtin_amdgcn_readfirstlane(wave_active ? min(min(wave_end, kt_hi) - kt_lo, T) - 1 : -1);
+  const int jw_last = __builtin_amdgcn_readfirstlane(wrows > 0 ? min(min(wave_end, kt_hi) - kt_lo, T) - 1 : -1);
 
-  // Q^T B operands: lane holds Q[row][16 s + 8 hf .. +7]; rows past the last
-  // stacked row read as zero.
+  // Q^T B operands: lane holds Q[row][16 s + 8 hf .. +7]; invalid rows read
+  // as zero (their offset lies past the buffer).  Waited for together with the
+  // first tiles' loads below.
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)rows_total * D * 2);
+  const uint32_t q_off = (uint32_t)(row_ok ? row : rows_total) * D * 2 + 16 * hf;
   bf16x8 qf[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(buf_ld16(rq, (uint32_t)row * D * 2 + 16 * hf + 32 * s, 0));
-  // Waited for here, on every path: the compiler's wait insertion then never
-  // sees these loads pending inside the loop, where a wait on them would also
-  // wait for the tile loads in flight.
-  wait_vm_loads();
+  for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(buf_ld16(rq, q_off + 32 * s, 0));
 
   // Direct loads (same unit map and swizzles as the kernel above).
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Skv * RB);
@@ -890,12 +931,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     for (int i = 0; i < PF; ++i) pre_v[i] = v_frag(Vs, i);
   };
   // Matrix phase: the P V MFMAs of the current tile (V slot Vs, P in pf),
-  // then the score MFMAs of the next tile (K slot Ks) into S.  P is dead
-  // before S is written, so the two never hold registers at once; the LDS
-  // reads run LA MFMAs ahead of their use.  After a wave's last tile the
-  // scores are computed from whatever the slot holds and never used: one code
-  // path keeps the compiler's register allocation of the loop simple.
-  auto matrix_phase = [&](const lds_t* Ks, const lds_t* Vs) __attribute__((always_inline)) {
+  // then, unless this is the wave's last tile (scores == false), the score
+  // MFMAs of the next tile (K slot Ks) into S.  P is dead before S is
+  // written, so the two never hold registers at once; the LDS reads run LA
+  // MFMAs ahead of their use (on the last tile the first LA - PF K reads are
+  // issued and left unused).  The two parts are scheduled as two regions.
+  auto matrix_phase = [&](const lds_t* Ks, const lds_t* Vs, bool scores) __attribute__((always_inline)) {
     if (o_pending) {   // rare: the vector phase raised the exponent base
 #pragma unroll
       for (int i = 0; i < DB; ++i)
@@ -912,21 +953,32 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
 #pragma unroll
     for (int t = PF; t < LA; ++t) fr[t] = frag(Ks, Vs, t);
 #pragma unroll
-    for (int t = 0; t < NT2; ++t) {
-      if (t + LA < NT2) fr[t + LA] = frag(Ks, Vs, t + LA);
-      if (t < NM) mfma_pv(fr[t], t);
-      else mfma_s(fr[t], t - NM);
+    for (int t = 0; t < NM; ++t) {
+      fr[t + LA] = frag(Ks, Vs, t + LA);
+      mfma_pv(fr[t], t);
     }
-    // Schedule: the reads of MFMAs PF .. LA - 1 first (two LDS reads for a
-    // V^T fragment, one for a K fragment), then each MFMA after the reads
-    // of the MFMA LA places later.
-    constexpr int lead = (LA <= NM ? 2 * (LA - PF) : 2 * (NM - PF) + (LA - NM));
+    // Schedule of each region: the reads of MFMAs PF .. LA - 1 first (two
+    // LDS reads for a V^T fragment, one for a K fragment), then each MFMA
+    // after the reads of the MFMA LA places later.
+    constexpr int lead = 2 * (LA - PF);
     if (lead > 0) __builtin_amdgcn_sched_group_barrier(0x100, lead, 0);
 #pragma unroll
-    for (int t = 0; t < NT2; ++t) {
+    for (int t = 0; t < NM; ++t) {
       if (t + LA < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else if (t + LA < NT2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if (scores) {
+#pragma unroll
+      for (int t = NM; t < NT2; ++t) {
+        if (t + LA < NT2) fr[t + LA] = frag(Ks, Vs, t + LA);
+        mfma_s(fr[t], t - NM);
+      }
+#pragma unroll
+      for (int t = NM; t < NT2; ++t) {
+        if (t + LA < NT2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -1012,17 +1064,22 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     else load_team(kt, vslot(slot));
   };
 
+  // Prologue: K(0..2) and V(0..1) in flight together with Q, one wait for
+  // all of them on every path (the compiler's wait insertion then never sees
+  // the Q loads pending inside the loop, where a wait on them would also wait
+  // for the tile loads in flight); S(0) and the exponent base (its row max)
+  // for every wave, then the softmax of tile 0.  Team 1 runs that softmax as
+  // its first half-step (beside team 0's first matrix phase) and loads V(2) in
+  // it; team 0 runs it before its first half-step.
   if (T > 0) {
-    // Prologue: K(0..2) and V(0..1) in flight together; S(0) and the exponent
-    // base (its row max) for every wave, then the softmax of tile 0.  Team 1
-    // runs that softmax as its first half-step (beside team 0's first matrix
-    // phase) and loads V(2) in it; team 0 runs it before its first half-step.
     load_k(kt_lo, kslot(IC<0>{}));
     if (T > 1) load_k(kt_lo + 1, kslot(IC<1>{}));
     if (T > 2) load_k(kt_lo + 2, kslot(IC<2>{}));
     load_v(kt_lo, vslot(IC<0>{}));
     if (T > 1) load_v(kt_lo + 1, vslot(IC<1>{}));
-    wait_vm_loads();
+  }
+  wait_vm_loads();
+  if (T > 0) {
     barrier();
     if (team == 1 && T > 2) load_team(kt_lo + 2, vslot(IC<2>{}));
     if (jw_last >= 0) {
@@ -1048,7 +1105,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   // tile.  JM = j % 3 names the slots.
   auto tile = [&](auto jm, int j) __attribute__((always_inline)) {
     constexpr int JM = decltype(jm)::value;
-    if (j <= jw_last) matrix_phase(kslot(IC<(JM + 1) % 3>{}), vslot(IC<JM>{}));
+    if (j <= jw_last) matrix_phase(kslot(IC<(JM + 1) % 3>{}), vslot(IC<JM>{}), j < jw_last);
     wait_vm_loads();
     barrier();
     if (j + 3 < T) load_ring(IC<JM>{}, kt_lo + j + 3);
@@ -1072,7 +1129,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_row = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
-  if (row < rows_total) {
+  if (row_ok) {
     const size_t flat = head0 * Sq + row;
     if (part_o != nullptr) {
       const size_t slot = flat * n_splits + tc.split;
@@ -1285,7 +1342,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     const long long wg8 = (rows + 255) / 256 * groups * a.n_splits;
     const bool eight = rows > 128 && wg8 >= kNumCUs;
     const bool paged = a.block_table != nullptr;
-    const long long nwg = eight ? wg8 : (rows + 127) / 128 * groups * a.n_splits;
+    // The two-team kernel's blocks are 32 positions x 8 query heads when G is
+    // a multiple of 8 (as many blocks as 256-row blocks whenever Sq % 32 == 0).
+    const int G = a.Hq / a.Hkv;
+    const long long wg_pp = (G % 8 == 0) ? (long long)(G / 8) * ((a.Sq + 31) / 32) * groups * a.n_splits : wg8;
+    const long long nwg = eight ? (paged ? wg8 : wg_pp) : (rows + 127) / 128 * groups * a.n_splits;
     const dim3 g((unsigned)nwg), blk_w(eight ? 512 : 256);
 #define SA_LAUNCH_ONE(DD, CC, WW, PG)                                                                    \
   hipLaunchKernelGGL((prefill_bf16_kernel<DD, CC, 1, WW, PG>), g, blk_w, 0, stream, (const bf16*)a.q,     \

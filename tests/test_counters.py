@@ -4,11 +4,11 @@ profiles/)."""
 
 # SQ_INSTS_MFMA of one 70B-shape causal prefill launch (B=1, 64/8 heads,
 # S=8192, d=128; two-team kernel), profiles/prefill_lds_mfma_counters_70b.md.
-MEASURED_PREFILL_MFMA = 34_078_720
+MEASURED_PREFILL_MFMA = 33_816_576
 # FETCH_SIZE and WRITE_SIZE (KiB per launch) of the same launch, and the
 # copy calibration (FETCH_SIZE reads half the bytes a plain copy moves,
 # WRITE_SIZE all of them), profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
-MEASURED_PREFILL_FETCH_KIB = 137_551
+MEASURED_PREFILL_FETCH_KIB = 137_288
 MEASURED_PREFILL_WRITE_KIB = 133_120
 FETCH_SCALE, WRITE_SCALE = 0.5, 1.0
 # FETCH_SIZE (KiB) of the decode split kernel and the KV bytes it must read.
@@ -24,19 +24,19 @@ PAGED_Q_BYTES = 16 * 64 * 4 * 128 * 2
 PREFILL_B, PREFILL_HQ, PREFILL_HKV, PREFILL_S, PREFILL_D = 1, 64, 8, 8192, 128
 
 
-def prefill_mfma_count(S, G, Hkv, rows_per_wg=256, waves=8, key_tile=64, d=128):
+def prefill_mfma_count(S, G, Hkv, rows_per_wave=32, key_tile=64, d=128):
     """MFMA instructions of a causal prefill (Sq = Skv = S) in the two-team
-    kernel: per wave, the scores of the first key tile, then one matrix phase
-    per key tile the wave sees (the P V product of that tile and the scores of
-    the next, computed even after the wave's last tile)."""
+    kernel.  A wave holds 32 positions of one query head (with G = 8 a
+    workgroup is the same 32 positions of the 8 heads) and computes, for
+    every key tile it sees, that tile's scores (the first in the prologue,
+    the others in the matrix phase before) and its P V product: the score
+    MFMAs of the tile after its last one are not issued."""
     per_tile = 2 * (d // 16)          # 32x32x16 MFMAs for 64 keys x 32 rows (scores), and as many for P V
-    rows = rows_per_wg // waves
     total = 0
     for _ in range(Hkv * G):
-        for t0 in range(0, S, rows_per_wg):
-            for w in range(waves):
-                tiles = -(-(t0 + rows * (w + 1)) // key_tile)   # causal: keys up to the wave's last row
-                total += per_tile + 2 * per_tile * tiles
+        for t0 in range(0, S, rows_per_wave):
+            tiles = -(-(t0 + rows_per_wave) // key_tile)   # causal: keys up to the wave's last row
+            total += 2 * per_tile * tiles
     return total
 
 
@@ -64,8 +64,8 @@ def test_prefill_hbm_traffic_stays_within_one_and_a_half_times_the_minimum():
 
 def test_prefill_kv_reads_share_the_group():
     """The G = 8 query heads of a KV head read its K/V tiles together (one
-    workgroup holds 256 stacked rows of one KV head), so the K/V bytes fetched
-    from memory stay far below one fetch per query head."""
+    workgroup holds the same 32 positions of all 8 heads), so the K/V bytes
+    fetched from memory stay far below one fetch per query head."""
     q, kv, _ = prefill_algorithmic_bytes()
     kv_fetched = MEASURED_PREFILL_FETCH_KIB * 1024 / FETCH_SCALE - q
     G = PREFILL_HQ // PREFILL_HKV
