@@ -74,36 +74,38 @@ def test_small_shapes(B, Hq, Hkv, Sq, Skv, d, causal, dtype):
     run_and_check(q, k, v, causal)
 
 
-def _full_size_check(w, per_block, num_splits=None):
+def _full_size_check(w, per_block, num_splits=None, block=32):
     """The workload at full size, in the launch the benchmark times: outputs
     start as NaN and must be finite everywhere afterwards (every M tile
     written), and in every query head ``per_block`` random rows of each
-    128-row block -- so every (head, 256-row M tile) of the 8-wave launch --
-    meet the bar against the oracle, with the relative Frobenius guard per
-    block."""
+    ``block``-position block meet the bar against the oracle, with the
+    relative Frobenius guard over the checked rows of each 128-row block.
+    With G = 8 a workgroup of the 8-wave launch holds 32 positions of the 8
+    query heads of a KV head, so 32-position blocks check every workgroup's
+    rows in every head."""
     q, k, v = W.prefill_inputs(w, DEV)
     o, lse = nan_outputs(q)
     sa.prefill(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, num_splits=num_splits)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "an output row was not written"
-    rows = block_rows(w.Sq, np.random.default_rng(w.seed), per_block=per_block)
+    rows = block_rows(w.Sq, np.random.default_rng(w.seed), block=block, per_block=per_block)
     return check_prefill_rows(o, lse, q, k, v, w.scale, w.causal, rows, what=f" {w.name}")
 
 
 def test_gqa70b_prefill_full_size_rows_of_every_tile():
-    """B=1, 64/8 heads, S=8192, d=128, causal: 2 rows of every 128-row block
-    of all 64 heads (8,320 rows) against the oracle."""
-    _full_size_check(W.GQA70B_PREFILL, per_block=2)
+    """B=1, 64/8 heads, S=8192, d=128, causal: one row of every 32-position
+    block of all 64 heads (16,448 rows) against the oracle."""
+    _full_size_check(W.GQA70B_PREFILL, per_block=1)
 
 
 def test_chunked_prefill_full_size_rows_of_every_tile():
     """512 new queries over a 65536-token prefix (bottom-right causal), in the
-    default split-KV launch and unsplit: 4 rows of every 128-row block of all
-    64 heads."""
+    default split-KV launch and unsplit: two rows of every 32-position block
+    of all 64 heads."""
     w = W.CHUNKED_PREFILL
     assert sa.prefill_splits(w.B, w.Hq, w.Hkv, w.Sq, w.Skv) == 2
-    _full_size_check(w, per_block=4)
-    _full_size_check(w, per_block=4, num_splits=1)
+    _full_size_check(w, per_block=2)
+    _full_size_check(w, per_block=2, num_splits=1)
 
 
 def test_skv_zero_noncausal_gives_zero_and_neg_inf():
@@ -278,14 +280,18 @@ def test_split_prefill_without_keys_gives_zero_and_neg_inf():
 
 
 # Shapes large enough for the 8-wave (256-row) workgroups, d = 64 and 128,
-# causal and not, checked on sampled rows (the small shapes above run the
-# 4-wave launch).
+# causal and not, checked on one sampled row of every 32-position block of
+# every head (the small shapes above run the 4-wave launch).  With G a
+# multiple of 8 a workgroup is 32 positions of 8 query heads, otherwise 256
+# consecutive stacked rows.
 EIGHT_WAVE = [
     # B, Hq, Hkv, Sq, Skv, d, causal
     (1, 32, 32, 2048, 2048, 64, False),
     (1, 64, 8, 1024, 1500, 128, False),
     (2, 16, 2, 2048, 2048, 64, True),
     (2, 40, 8, 1000, 1000, 128, True),     # G = 5: row blocks straddle query heads, ragged last block
+    (2, 64, 4, 1000, 1000, 128, True),     # G = 16: two blocks of 8 heads per KV head, ragged last positions
+    (2, 32, 4, 1000, 1300, 64, True),      # G = 8, d = 64: ragged last positions, queries after a 300-key prefix
 ]
 
 
@@ -301,7 +307,7 @@ def test_eight_wave_launch_rows_of_every_tile(B, Hq, Hkv, Sq, Skv, d, causal):
     sa.prefill(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "an output row was not written"
-    rows = sorted(set(block_rows(Sq, np.random.default_rng(Sq + Skv), per_block=2)) | {1, 127, 128, 255, 256})
+    rows = sorted(set(block_rows(Sq, np.random.default_rng(Sq + Skv), block=32)) | {1, 127, 128, 255, 256})
     check_prefill_rows(o, lse, q, k, v, scale, causal, rows)
 
 
