@@ -292,6 +292,8 @@ EIGHT_WAVE = [
     (2, 40, 8, 1000, 1000, 128, True),     # G = 5: row blocks straddle query heads, ragged last block
     (2, 64, 4, 1000, 1000, 128, True),     # G = 16: two blocks of 8 heads per KV head, ragged last positions
     (2, 32, 4, 1000, 1300, 64, True),      # G = 8, d = 64: ragged last positions, queries after a 300-key prefix
+    (32, 64, 8, 20, 20, 128, True),        # G = 8, one partial 32-position block (20 rows per wave)
+    (1, 96, 4, 700, 700, 128, True),       # G = 24: three blocks of 8 heads per KV head, ragged last positions
 ]
 
 
@@ -307,7 +309,8 @@ def test_eight_wave_launch_rows_of_every_tile(B, Hq, Hkv, Sq, Skv, d, causal):
     sa.prefill(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "an output row was not written"
-    rows = sorted(set(block_rows(Sq, np.random.default_rng(Sq + Skv), block=32)) | {1, 127, 128, 255, 256})
+    rows = sorted(r for r in set(block_rows(Sq, np.random.default_rng(Sq + Skv), block=32)) | {1, 127, 128, 255, 256}
+                  if r < Sq)
     check_prefill_rows(o, lse, q, k, v, scale, causal, rows)
 
 
