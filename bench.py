@@ -57,12 +57,12 @@ METRIC = "prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak), 70B-shape GQ
 FETCH_SCALE = 0.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "1a8daa9ba4368b38",
-                "fetch_kib": 137288, "write_kib": 133120},
+    "prefill": {"sources": ["common.h", "prefill.hip"], "sha256_16": "ddc01e2fae5a9f54",
+                "fetch_kib": 137339, "write_kib": 133120},
     "decode": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "05ddfcb1dded8f23",
                "fetch_kib": 262253 + 4170, "write_kib": 8256 + 65},
-    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "e5e68cae69aed347",
-                "fetch_kib": 140447 + 16914, "write_kib": 33280 + 8448},
+    "chunked": {"sources": ["common.h", "prefill.hip", "combine.hip"], "sha256_16": "4739eee8bdee01c4",
+                "fetch_kib": 140440 + 16914, "write_kib": 33280 + 8448},
     "paged": {"sources": ["common.h", "paged.hip", "combine.hip"], "sha256_16": "f2459d9c52b18dfe",
               "fetch_kib": 574406 + 6258, "write_kib": 12391 + 1056},
     "ragged": {"sources": ["common.h", "decode.hip", "combine.hip"], "sha256_16": "05ddfcb1dded8f23",

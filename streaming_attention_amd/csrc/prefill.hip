@@ -404,17 +404,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 - QB : 1) void prefill_bf16_ke
   // raised, O and l rescaled by 2^(m_old - m_new) and P recomputed.  Data
   // whose scores never climb far above the first tile's maximum never takes
   // that path.
+  // Key kt kBN + 4 hf + o (o = 32 kb + 8 (r / 4) + r % 4, at most 59) is
+  // visible when o <= lim: one compare of a lane value with a small constant
+  // per element.
   auto mask_tile = [&](int kt, f32x16 (&S)[QB][2]) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int last = CAUSAL ? min(pos[qb], Skv - 1) : Skv - 1;
+      const int lim = last - kt * kBN - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = (key < Skv) && (!CAUSAL || key <= pos[qb]);
-          S[qb][kb][r] = vis ? S[qb][kb][r] : kNegInf;
+          const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+          S[qb][kb][r] = (o <= lim) ? S[qb][kb][r] : kNegInf;
         }
+    }
   };
   auto exponentiate = [&](f32x16 (&S)[QB][2], float (&psum)[QB]) {
 #pragma unroll
@@ -983,14 +988,18 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // Key kt kBN + 4 hf + o (o = 32 kb + 8 (r / 4) + r % 4, at most 59) is
+  // visible when o <= lim: one compare of a lane value with a small constant
+  // per element.
   auto mask_tile = [&](int kt) __attribute__((always_inline)) {
+    const int last = CAUSAL ? min(pos, Skv - 1) : Skv - 1;
+    const int lim = last - kt * kBN - 4 * hf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kt * kBN + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const bool vis = (key < Skv) && (!CAUSAL || key <= pos);
-        S[kb][r] = vis ? S[kb][r] : kNegInf;
+        const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+        S[kb][r] = (o <= lim) ? S[kb][r] : kNegInf;
       }
   };
   auto tile_needs_mask = [&](int kt) __attribute__((always_inline)) {

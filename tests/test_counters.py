@@ -8,7 +8,7 @@ MEASURED_PREFILL_MFMA = 33_816_576
 # FETCH_SIZE and WRITE_SIZE (KiB per launch) of the same launch, and the
 # copy calibration (FETCH_SIZE reads half the bytes a plain copy moves,
 # WRITE_SIZE all of them), profiles/hbm_traffic_70b_prefill_decode_chunked_paged.md.
-MEASURED_PREFILL_FETCH_KIB = 137_288
+MEASURED_PREFILL_FETCH_KIB = 137_339
 MEASURED_PREFILL_WRITE_KIB = 133_120
 FETCH_SCALE, WRITE_SCALE = 0.5, 1.0
 # FETCH_SIZE (KiB) of the decode split kernel and the KV bytes it must read.
