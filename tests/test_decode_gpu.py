@@ -170,6 +170,34 @@ def test_combine_fp32_output_and_random_partials():
         assert_lse(lse[b], L_ref, "f32")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_combine_few_splits_per_sequence_counts(d, out_dtype):
+    """The merge for at most 8 splits (one wave per row) on arbitrary partials:
+    per-sequence counts 1..8 out of 8 slots, -inf entries, a row with every
+    split empty; against the oracle's log-sum-exp merge of the first n_b
+    slots (slots past n_b hold values that must not count)."""
+    rng = np.random.default_rng(11 + d)
+    B, Hq, S = 9, 6, 8
+    lse_p = rng.normal(0.0, 3.0, (B, Hq, S))
+    lse_p[1, 2, :3] = -np.inf
+    lse_p[4, 0, :] = -np.inf
+    o_p = rng.standard_normal((B, Hq, S, d))
+    po = torch.tensor(o_p, dtype=torch.float32, device=DEV)
+    pl = torch.tensor(lse_p, dtype=torch.float32, device=DEV)
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 8]
+    ns = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    o, lse = sa.combine_lse(po, pl, ns, out_dtype)
+    torch.cuda.synchronize()
+    kind = "f32" if out_dtype == torch.float32 else "bf16"
+    for b in range(B):
+        n = counts[b]
+        L_ref, O_ref = oracle.merge_partials(np.moveaxis(f64(pl[b, :, :n]), 1, 0),
+                                             np.moveaxis(f64(po[b, :, :n]), 1, 0))
+        assert_o(o[b, :, 0], O_ref, kind)
+        assert_lse(lse[b], L_ref, "f32")
+
+
 def test_decode_matches_last_row_of_prefill_oracle():
     """Decode over len keys == the last row of a causal prefill over them."""
     S, d = 1500, 128
