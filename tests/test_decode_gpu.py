@@ -42,6 +42,44 @@ def _check_partials(part_o, part_lse, q, k, v, lens, nsplits, scale, seqs, split
             assert_lse(part_lse[b, :, s], L_ref, "bf16", f"partial LSE seq {b} split {s}")
 
 
+def _decode_sweep(n, seed):
+    """Decode shapes from a seeded generator: batch 1-5, 1-4 KV heads, group
+    sizes up to 16, d = 64 or 128, cache capacities that are rarely chunk
+    multiples, 1 to 64 split slots, and a seed for the per-sequence lengths
+    (0 included) and split counts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, Hkv = int(rng.integers(1, 6)), int(rng.integers(1, 5))
+        G = int(rng.choice([1, 2, 4, 5, 8, 16]))
+        out.append((B, G * Hkv, Hkv, int(rng.integers(1, 3000)), int(rng.choice([64, 128])),
+                    int(rng.choice([1, 3, 8, 17, 64])), int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,S_cap,d,max_splits,seed", _decode_sweep(16, 91))
+def test_decode_seeded_sweep(B, Hq, Hkv, S_cap, d, max_splits, seed, fused):
+    """Random decode shapes, per-sequence lengths (some 0) and split counts,
+    split + merge and the one-launch form: every sequence and head against
+    the oracle."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(0, S_cap + 1, B)]
+    if B > 1:
+        lens[int(rng.integers(0, B))] = S_cap
+    ns = [int(x) for x in rng.integers(1, max_splits + 1, B)]
+    g = torch.Generator(device=DEV).manual_seed(seed % 100000)
+    q = torch.randn((B, Hq, 1, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S_cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    kv_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    nsp = torch.tensor(ns, dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(d)
+    o, lse = sa.decode(q, k, v, kv_len, nsp, max_splits=max_splits, scale=scale, fused=fused)
+    torch.cuda.synchronize()
+    _check_rows(o, lse, q, k, v, lens, scale, range(B))
+
+
 def test_gqa70b_decode_full_size():
     """B=4, 64/8 heads, 32768 keys each, 64 splits: every output row and a
     sample of split partials, in the benchmark's launch shape."""

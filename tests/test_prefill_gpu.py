@@ -74,6 +74,67 @@ def test_small_shapes(B, Hq, Hkv, Sq, Skv, d, causal, dtype):
     run_and_check(q, k, v, causal)
 
 
+def _sweep_shapes(n, seed, large=False):
+    """Shapes drawn from a seeded generator: batch 1-2, 1-3 KV heads (8 for the
+    large ones), group sizes 1, 2, 4, 5 or 8, d = 64 or 128, causal or not,
+    lengths that are rarely tile multiples.  Large shapes give at least 256
+    workgroups of 256 rows, so the 8-wave (two-team) launch runs."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        if large:
+            B, Hkv, G = int(rng.integers(1, 3)), 8, int(rng.choice([1, 4, 8]))
+            Sq = int(rng.integers(600, 1400))
+            if -(-G * Sq // 256) * B * Hkv < 256:
+                continue
+            Skv = int(rng.integers(Sq if causal else 300, 1600))
+        else:
+            B, Hkv, G = int(rng.integers(1, 3)), int(rng.choice([1, 2, 3])), int(rng.choice([1, 2, 4, 5, 8]))
+            Sq = int(rng.integers(1, 260))
+            Skv = int(rng.integers(Sq if causal else 1, 520))
+        out.append((B, G * Hkv, Hkv, Sq, Skv, d, causal))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal", _sweep_shapes(40, 77))
+def test_seeded_shape_sweep(B, Hq, Hkv, Sq, Skv, d, causal):
+    """Random shapes of the default launch, every output element against the
+    oracle; every third shape also through two or three key splits and the
+    merge."""
+    g = torch.Generator(device=DEV).manual_seed(5000 + B * 7 + Hq * 13 + Sq + 3 * Skv + d)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    o, lse = run_and_check(q, k, v, causal)
+    if (Sq + Skv) % 3 == 0:
+        n = 2 + (Sq + Skv) % 2
+        o2, lse2 = sa.prefill(q, k, v, causal=causal, num_splits=n)
+        torch.cuda.synchronize()
+        O_ref, L_ref = oracle.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(d), causal)
+        assert_o(o2, O_ref, "bf16", f"O ({n} splits)")
+        assert_lse(lse2, L_ref, "bf16", f"LSE ({n} splits)")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal", _sweep_shapes(10, 78, large=True))
+def test_seeded_shape_sweep_eight_wave(B, Hq, Hkv, Sq, Skv, d, causal):
+    """Random shapes of the 8-wave launch: outputs start as NaN and must all be
+    written; one row of every 32-position block of every head against the
+    oracle."""
+    g = torch.Generator(device=DEV).manual_seed(6000 + B * 7 + Hq * 13 + Sq + 3 * Skv + d)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = nan_outputs(q)
+    sa.prefill(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "an output row was not written"
+    rows = sorted(r for r in set(block_rows(Sq, np.random.default_rng(Sq + Skv), block=32)) | {0, Sq - 1})
+    check_prefill_rows(o, lse, q, k, v, scale, causal, rows)
+
+
 def _full_size_check(w, per_block, num_splits=None, block=32):
     """The workload at full size, in the launch the benchmark times: outputs
     start as NaN and must be finite everywhere afterwards (every M tile
