@@ -66,6 +66,36 @@ def test_paged_decode_small(B, Hq, Hkv, T_q, lens, d, splits):
     _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(B))
 
 
+def _paged_sweep(n, seed):
+    """Paged decode shapes from a seeded generator: batch 1-6, 1-4 KV heads,
+    group sizes up to 16, 1-24 query tokens (both kernels: up to 32 and
+    beyond 32 stacked rows), d = 64 or 128, lengths 0-1500 (some shorter than
+    the query block), split counts 1-9 or the binding's choice, and keys per
+    split for some."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, Hkv = int(rng.integers(1, 7)), int(rng.integers(1, 5))
+        G, T_q = int(rng.choice([1, 2, 4, 8, 16])), int(rng.choice([1, 2, 3, 4, 7, 16, 24]))
+        lens = [int(x) for x in rng.integers(0, 1501, B)]
+        splits = [None, 1, 2, 3, 6, 9][int(rng.integers(0, 6))]
+        kps = int(rng.choice([256, 700])) if splits is None and rng.integers(0, 2) else None
+        out.append((B, G * Hkv, Hkv, T_q, lens, int(rng.choice([64, 128])), splits, kps))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T_q,lens,d,splits,kps", _paged_sweep(24, 93))
+def test_paged_decode_seeded_sweep(B, Hq, Hkv, T_q, lens, d, splits, kps):
+    """Random paged decodes (shuffled pages, NaN past every length and in the
+    spare pages): every sequence, head and token against the oracle."""
+    w = dataclasses.replace(W.PAGED_DECODE, B=B, Hq=Hq, Hkv=Hkv, T_q=T_q, d=d, seed=300 + sum(lens) + T_q)
+    q, kp, vp, table, lens_t = W.paged_inputs(w, DEV, lengths=torch.tensor(lens))
+    o, lse = sa.decode_paged(q, kp, vp, table.to(DEV), lens_t.to(DEV), num_splits=splits, scale=w.scale,
+                             keys_per_split=kps)
+    torch.cuda.synchronize()
+    _check(o, lse, q, kp, vp, table, lens_t, w.scale, range(B))
+
+
 def test_paged_decode_matches_contiguous_decode_for_one_token():
     """T_q = 1 over pages == attn_decode_splitkv + merge over the same keys laid
     out contiguously."""
