@@ -117,6 +117,16 @@ def test_seeded_shape_sweep(B, Hq, Hkv, Sq, Skv, d, causal):
         assert_lse(lse2, L_ref, "bf16", f"LSE ({n} splits)")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal", _sweep_shapes(10, 79))
+def test_seeded_shape_sweep_f32(B, Hq, Hkv, Sq, Skv, d, causal):
+    """Random shapes on the fp32 path, every output element at 1e-4."""
+    g = torch.Generator(device=DEV).manual_seed(7000 + B * 7 + Hq * 13 + Sq + 3 * Skv + d)
+    q = torch.randn((B, Hq, Sq, d), generator=g, device=DEV)
+    k = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV)
+    v = torch.randn((B, Hkv, Skv, d), generator=g, device=DEV)
+    run_and_check(q, k, v, causal)
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d,causal", _sweep_shapes(10, 78, large=True))
 def test_seeded_shape_sweep_eight_wave(B, Hq, Hkv, Sq, Skv, d, causal):
     """Random shapes of the 8-wave launch: outputs start as NaN and must all be
