@@ -28,7 +28,8 @@ def f64(t) -> np.ndarray:
 def max_abs(a, b) -> float:
     a, b = f64(a), f64(b)
     same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    err = np.where(same_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):   # inf - inf where both are the same infinity: masked out here
+        err = np.where(same_inf, 0.0, np.abs(a - b))
     if not np.all(np.isfinite(err)):
         return float("inf")
     return float(err.max()) if err.size else 0.0
